@@ -1,0 +1,327 @@
+"""Seeded synthetic inputs for fused graph sparse attention.
+
+This module produces graphs (as COO edge lists, source -> destination) and
+random node/edge feature tensors. It holds none of the attention arithmetic
+and none of the CSR / row-window construction: both the CPU oracle and the
+HIP library consume exactly what this module returns.
+
+Seeding: every random stream is ``numpy.random.Generator(PCG64(SeedSequence
+([config, stream, seed])))`` with stream 0 = graph, 1 = Q, 2 = K, 3 = V,
+4 = E, 5 = edge-order shuffle of the small fuzz graphs.
+
+Edge order: the five workloads hand over their COO list grouped by source
+(ascending source, then destination), the COO "row = source" layout of the
+gattn-triton article's CSC section; building the destination-grouped CSR
+from it is real work.  Fuzz graphs use a random edge order.  Q/K/V/E are drawn as float32 N(0, 1);
+fp16 / bf16 workloads round those values to nearest-even (``cast``).
+
+The five workloads restate the sizes and structure of the pages' problems:
+
+1. random graph, N=320, in-degree ~ Poisson(14), distinct uniform sources,
+   H=8, D=32, fp32, standard softmax (the size used by the CSR aggregation
+   problem on the POPCORNBENCH page);
+2. RTMScore-style batch: 64 molecular-like graphs, n ~ U{100..300} points
+   in a 20 A cube, in-edges from the 10 nearest neighbours, H=8, D=16, fp32
+   with an edge projection E, clipped softmax (the gattn-triton article's
+   "Background" and "Fusing the full graph attention" sections; batch 64 is
+   its headline table);
+3. single power-law graph, N=169,343, Zipf(2.1) in-degree truncated to
+   [1, 2000], preferential-attachment sources, H=1, D=64, fp16;
+4. large power-law graph, N=2.45M, lognormal(3.0, 1.2) in-degree truncated
+   to [1, 5000], uniform sources, H=1, D=64, bf16;
+5. 1024 complete digraphs (self-loops included), n ~ U{20..40}, H=8, D=64,
+   fp16 (near-dense 16-row windows, the Fused3S regime).
+
+Configs 3-5 use the standard softmax of the Fused3S abstract.  The degree
+laws of configs 3 and 4 are used as written; the realised edge count is
+whatever they produce.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+STREAM_GRAPH, STREAM_Q, STREAM_K, STREAM_V, STREAM_E, STREAM_ORDER = range(6)
+
+
+def rng_for(config: int, stream: int, seed: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([config, stream, seed])))
+
+
+@dataclasses.dataclass
+class Workload:
+    config: int
+    name: str
+    num_nodes: int
+    src: np.ndarray          # int32 [nnz], COO source
+    dst: np.ndarray          # int32 [nnz], COO destination
+    heads: int
+    head_dim: int
+    dtype: str               # "f32" | "f16" | "bf16"
+    mode: str                # "standard" | "clipped"
+    has_e: bool
+    clip: tuple = (-5.0, 5.0)
+    eps: float = 1e-6
+    seed: int = 0
+
+    @property
+    def nnz(self) -> int:
+        return int(self.src.shape[0])
+
+    @property
+    def scale(self) -> float:
+        # 1/sqrt(D), rounded once to float32; both sides receive this value.
+        return float(np.float32(1.0 / math.sqrt(self.head_dim)))
+
+    def node_tensor(self, stream: int) -> np.ndarray:
+        """float32 N(0,1) tensor [N, H, D] for stream Q/K/V."""
+        g = rng_for(self.config, stream, self.seed)
+        return g.standard_normal((self.num_nodes, self.heads, self.head_dim), dtype=np.float32)
+
+    def q(self):
+        return self.node_tensor(STREAM_Q)
+
+    def k(self):
+        return self.node_tensor(STREAM_K)
+
+    def v(self):
+        return self.node_tensor(STREAM_V)
+
+    def e(self) -> Optional[np.ndarray]:
+        """float32 N(0,1) edge tensor [nnz, H, D], indexed by CSR position."""
+        if not self.has_e:
+            return None
+        g = rng_for(self.config, STREAM_E, self.seed)
+        return g.standard_normal((self.nnz, self.heads, self.head_dim), dtype=np.float32)
+
+
+def cast(x: np.ndarray, dtype: str):
+    """Round a float32 array to the workload dtype; returns a CPU torch tensor."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to({"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype])
+
+
+# ---------------------------------------------------------------------------
+# graph generators
+# ---------------------------------------------------------------------------
+
+def _order_by_source(src, dst, n):
+    """COO sorted by (source, destination)."""
+    key = src.astype(np.int64)
+    key *= n
+    key += dst
+    key.sort()
+    s = np.floor_divide(key, n)
+    key -= s * n
+    return np.ascontiguousarray(s.astype(np.int32)), np.ascontiguousarray(key.astype(np.int32))
+
+
+def _shuffle(config, seed, src, dst):
+    g = rng_for(config, STREAM_ORDER, seed)
+    perm = g.permutation(src.shape[0])
+    return np.ascontiguousarray(src[perm].astype(np.int32)), np.ascontiguousarray(dst[perm].astype(np.int32))
+
+
+def _distinct_uniform_sources(g, deg, n):
+    """For each destination i, deg[i] distinct sources drawn uniformly from
+    [0, n) (self allowed).  Vectorised: draw with replacement, then redraw
+    repeated (dst, src) pairs until none remain."""
+    deg = deg.astype(np.int64)
+    dst = np.repeat(np.arange(n, dtype=np.int64), deg)
+    key = g.integers(0, n, size=dst.shape[0], dtype=np.int64)
+    key += dst * n
+    key.sort()
+    dup = np.flatnonzero(key[1:] == key[:-1]) + 1
+    if dup.size:
+        # few repeats (about sum(d^2)/2n); redraw each until it is new in its row
+        row_ptr = np.zeros(n + 1, dtype=np.int64)
+        np.cumsum(deg, out=row_ptr[1:])
+        taken = {}
+        repl = []
+        for p in dup.tolist():
+            i = int(key[p] // n)
+            seg = key[row_ptr[i]:row_ptr[i + 1]]          # still sorted: edits applied below
+            extra = taken.setdefault(i, set())
+            while True:
+                s = int(g.integers(0, n))
+                kk = i * n + s
+                j = int(np.searchsorted(seg, kk))
+                if (j < seg.shape[0] and seg[j] == kk) or kk in extra:
+                    continue
+                extra.add(kk)
+                repl.append((p, kk))
+                break
+        for p, kk in repl:
+            key[p] = kk
+    dst *= n
+    key -= dst
+    dst //= n
+    return key, dst
+
+
+def gen_config1(seed=0) -> Workload:
+    n = 320
+    g = rng_for(1, STREAM_GRAPH, seed)
+    deg = np.minimum(g.poisson(14.0, size=n), n)
+    srcs, dsts = [], []
+    for i in range(n):
+        s = g.choice(n, size=int(deg[i]), replace=False)
+        srcs.append(s)
+        dsts.append(np.full(s.shape[0], i))
+    src = np.concatenate(srcs) if srcs else np.zeros(0, np.int64)
+    dst = np.concatenate(dsts) if dsts else np.zeros(0, np.int64)
+    src, dst = _order_by_source(src, dst, n)
+    return Workload(1, "random graph N=320 Poisson(14) H=8 D=32 fp32 standard", n, src, dst,
+                    8, 32, "f32", "standard", False, seed=seed)
+
+
+def knn_graph_batch(g, num_graphs, n_lo, n_hi, k, box):
+    """Batched point clouds; in-edges of each node from its k nearest other
+    nodes of the same graph (squared Euclidean distance in fp64, ties to the
+    lower index); block-diagonal numbering."""
+    srcs, dsts = [], []
+    off = 0
+    for _ in range(num_graphs):
+        n = int(g.integers(n_lo, n_hi + 1))
+        p = g.random((n, 3)) * box
+        d2 = ((p[:, None, :] - p[None, :, :]) ** 2).sum(-1)
+        np.fill_diagonal(d2, np.inf)
+        nb = np.argsort(d2, axis=1, kind="stable")[:, :k]          # [n, k] sources of node i
+        dsts.append(np.repeat(np.arange(n), k) + off)
+        srcs.append(nb.reshape(-1) + off)
+        off += n
+    return off, np.concatenate(srcs), np.concatenate(dsts)
+
+
+def gen_config2(seed=0, num_graphs=64) -> Workload:
+    g = rng_for(2, STREAM_GRAPH, seed)
+    n, src, dst = knn_graph_batch(g, num_graphs, 100, 300, 10, 20.0)
+    src, dst = _order_by_source(src, dst, n)
+    return Workload(2, "RTMScore batch 64 graphs kNN10 H=8 D=16 fp32 clipped+E", n, src, dst,
+                    8, 16, "f32", "clipped", True, seed=seed)
+
+
+def _zipf_truncated(g, a, lo, hi, size):
+    out = g.zipf(a, size=size)
+    bad = (out < lo) | (out > hi)
+    while bad.any():
+        out[bad] = g.zipf(a, size=int(bad.sum()))
+        bad = (out < lo) | (out > hi)
+    return out.astype(np.int64)
+
+
+def preferential_sources(g, deg):
+    """Destinations in index order; destination i draws deg[i] distinct
+    sources != i from an urn where node j has weight (times j was already
+    chosen + 1).  A draw takes floor(u * urn_size) of a uniform u; entries
+    below n are the +1 base weights, later entries are earlier choices."""
+    n = deg.shape[0]
+    total = int(deg.sum())
+    urn = np.empty(n + total, dtype=np.int64)
+    urn[:n] = np.arange(n)
+    size = n
+    src = np.empty(total, dtype=np.int64)
+    pos = 0
+    buf = g.random(2 * total + 1024)
+    bi = 0
+    urn_l = urn  # local alias
+    for i in range(n):
+        d = int(deg[i])
+        chosen = set()
+        while len(chosen) < d:
+            if bi >= buf.shape[0]:
+                buf = g.random(total + 1024)
+                bi = 0
+            j = int(urn_l[int(buf[bi] * size)])
+            bi += 1
+            if j == i or j in chosen:
+                continue
+            chosen.add(j)
+            src[pos] = j
+            pos += 1
+            urn_l[size] = j
+            size += 1
+    dst = np.repeat(np.arange(n, dtype=np.int64), deg)
+    return src, dst
+
+
+def gen_config3(seed=0, n=169_343) -> Workload:
+    g = rng_for(3, STREAM_GRAPH, seed)
+    deg = _zipf_truncated(g, 2.1, 1, min(2000, n - 1), n)
+    src, dst = preferential_sources(g, deg)
+    src, dst = _order_by_source(src, dst, n)
+    return Workload(3, f"power-law Zipf(2.1) N={n} pref-attach H=1 D=64 fp16 standard", n, src, dst,
+                    1, 64, "f16", "standard", False, seed=seed)
+
+
+def _lognormal_degrees(g, mu, sigma, lo, hi, size):
+    d = np.rint(g.lognormal(mu, sigma, size=size))
+    bad = (d < lo) | (d > hi)
+    while bad.any():
+        d[bad] = np.rint(g.lognormal(mu, sigma, size=int(bad.sum())))
+        bad = (d < lo) | (d > hi)
+    return d.astype(np.int64)
+
+
+def gen_config4(seed=0, n=2_450_000) -> Workload:
+    g = rng_for(4, STREAM_GRAPH, seed)
+    deg = _lognormal_degrees(g, 3.0, 1.2, 1, min(5000, n), n)
+    src, dst = _distinct_uniform_sources(g, deg, n)
+    src, dst = _order_by_source(src, dst, n)
+    return Workload(4, f"power-law lognormal(3,1.2) N={n} uniform sources H=1 D=64 bf16 standard", n,
+                    src, dst, 1, 64, "bf16", "standard", False, seed=seed)
+
+
+def complete_graph_batch(g, num_graphs, n_lo, n_hi):
+    srcs, dsts = [], []
+    off = 0
+    for _ in range(num_graphs):
+        n = int(g.integers(n_lo, n_hi + 1))
+        a = np.arange(n) + off
+        srcs.append(np.tile(a, n))
+        dsts.append(np.repeat(a, n))
+        off += n
+    return off, np.concatenate(srcs), np.concatenate(dsts)
+
+
+def gen_config5(seed=0, num_graphs=1024) -> Workload:
+    g = rng_for(5, STREAM_GRAPH, seed)
+    n, src, dst = complete_graph_batch(g, num_graphs, 20, 40)
+    src, dst = _order_by_source(src, dst, n)
+    return Workload(5, "1024 complete digraphs n~U{20..40} H=8 D=64 fp16 standard", n, src, dst,
+                    8, 64, "f16", "standard", False, seed=seed)
+
+
+GENERATORS = {1: gen_config1, 2: gen_config2, 3: gen_config3, 4: gen_config4, 5: gen_config5}
+
+
+def make(config: int, seed: int = 0, **kw) -> Workload:
+    return GENERATORS[config](seed=seed, **kw)
+
+
+def random_graph(config_tag, seed, n, deg_max, allow_self=True, multi=False):
+    """Small fuzz graphs for tests: in-degree ~ U{0..deg_max}; distinct
+    sources unless ``multi``; returns (src, dst) int32 shuffled."""
+    g = rng_for(config_tag, STREAM_GRAPH, seed)
+    srcs, dsts = [], []
+    for i in range(n):
+        d = int(g.integers(0, deg_max + 1))
+        pool = n if allow_self else n - 1
+        if pool <= 0:
+            continue
+        if multi:
+            s = g.integers(0, pool, size=d)
+        else:
+            s = g.choice(pool, size=min(d, pool), replace=False)
+        if not allow_self:
+            s = np.where(s >= i, s + 1, s)
+        srcs.append(s)
+        dsts.append(np.full(s.shape[0], i))
+    if not srcs:
+        return np.zeros(0, np.int32), np.zeros(0, np.int32)
+    src, dst = np.concatenate(srcs), np.concatenate(dsts)
+    return _shuffle(config_tag, seed, src, dst)
