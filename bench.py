@@ -1,0 +1,321 @@
+"""Benchmark of the fused graph attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+A step is one pass of the whole path over one batch of synthetic input:
+gattn_build_csr (COO -> CSR on the device) followed by gattn_forward (the
+fused SDDMM / softmax / SpMM).  The default workload is the RTMScore-style
+batch of 64 kNN graphs (8 heads x 16, fp32, clipped softmax with an edge
+projection), the setting of the gattn-triton article's headline table.
+
+Honest HBM numbers: the step cycles through R copies of the batch whose
+total size is well above the 256 MB Infinity Cache, so every step streams
+its inputs from HBM.  Before the timed region a sleep kernel holds the GPU
+while the host enqueues all K steps, so the GPU then runs them back to back
+and the HIP events around each kernel measure the kernel, not host gaps.
+
+Output: one JSON line (metric, value in GEdges/s of the whole step, roofline
+of the forward kernel against 8 TB/s HBM, the CPU oracle's rate on the host).
+
+Counter mode (used under rocprofv3 --pmc):
+    python bench.py --counters-run        one copy kernel of known size, then
+                                          forward launches, no timing
+    python bench.py --ingest-counters DIR summarise rocprofv3 CSVs into
+                                          profiles/<kernel>_<workload>_counters.json
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused graph attention GEdges/s at 1 MI355X; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = {"gather": "graph_sparse_attention_amd/csrc/forward_gather.hip",
+              "mfma": "graph_sparse_attention_amd/csrc/forward_mfma.hip"}
+COPY_BYTES = 512 << 20      # calibration copy for the traffic counters
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", type=int, default=2)
+    p.add_argument("--path", default="auto", choices=["auto", "gather", "mfma"])
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="bound of the CPU oracle sample")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--counters-run", action="store_true")
+    p.add_argument("--ingest-counters", default=None)
+    return p.parse_args()
+
+
+def src_hash(path_key):
+    with open(os.path.join(ROOT, KERNEL_SRC[path_key]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# workload and algorithmic bytes
+# ---------------------------------------------------------------------------
+
+def algorithmic_bytes(n, nnz, h, d, s, has_e):
+    """Compulsory HBM bytes of one forward: every input once, output once.
+    B_min = 4(N+1) + 4 nnz + 3 N H D s + nnz H D s [E] + N H D s."""
+    return 4 * (n + 1) + 4 * nnz + 3 * n * h * d * s + (nnz * h * d * s if has_e else 0) + n * h * d * s
+
+
+class Batch:
+    def __init__(self, wl, dev, host):
+        import torch
+        import graph_sparse_attention_amd as gsa
+        self.src = host["src"].to(dev)
+        self.dst = host["dst"].to(dev)
+        self.q, self.k, self.v = (host[x].to(dev) for x in ("q", "k", "v"))
+        self.e = host["e"].to(dev) if host["e"] is not None else None
+        self.out = torch.empty_like(self.q)
+        self.csr = gsa.CsrBuilder(wl.num_nodes, wl.nnz, dev)
+        self.rw = None
+
+
+def make_host_inputs(wl):
+    import torch
+    import workloads as W
+    h = {"src": torch.from_numpy(wl.src), "dst": torch.from_numpy(wl.dst)}
+    for x in ("q", "k", "v"):
+        h[x] = W.cast(getattr(wl, x)(), wl.dtype)
+    h["e"] = W.cast(wl.e(), wl.dtype) if wl.has_e else None
+    return h
+
+
+def batch_bytes(wl, es):
+    n, m, hd = wl.num_nodes, wl.nnz, wl.heads * wl.head_dim
+    return 8 * m + 4 * n + 8 * m + 4 * n * hd * es + (m * hd * es if wl.has_e else 0)
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(wl, host, seconds):
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    q64, k64, v64 = (oracle.widen(host[x]) for x in ("q", "k", "v"))
+    e64 = oracle.widen(host["e"]) if host["e"] is not None else None
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        rp, ci, pe = oracle.build_csr(wl.num_nodes, wl.src, wl.dst)
+        oracle.forward(rp, ci, q64, k64, v64, e64, mode=wl.mode, scale=wl.scale, clip=wl.clip, eps=wl.eps,
+                       threads=cores)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(wl.nnz * reps / el / 1e9, 6), "unit": "GEdges/s", "cores": cores, "kind": "oracle",
+            "sample": f"the full batch ({wl.nnz} edges), oracle CSR build (1 thread) + fp64 forward "
+                      f"({cores} OpenMP threads), repeated {reps}x in {el:.1f} s; host CPU: {cpu_model}"}
+
+
+# ---------------------------------------------------------------------------
+# counters
+# ---------------------------------------------------------------------------
+
+def counters_file(path_key, config):
+    return os.path.join(PROFILES, f"{'forward_gather' if path_key == 'gather' else 'forward_mfma'}_config{config}_counters.json")
+
+
+def load_traffic(path_key, config):
+    f = counters_file(path_key, config)
+    if not os.path.exists(f):
+        return None
+    d = json.load(open(f))
+    if d.get("kernel_source_sha256_16") != src_hash(path_key):
+        return None           # the kernel changed since the counters were taken
+    return d
+
+
+def ingest_counters(dirname, config, path_key):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the forward kernel
+    and of the calibration copy; scale by the copy's bytes-per-count."""
+    rows = []
+    import csv
+    for f in glob.glob(os.path.join(dirname, "**", "*counter_collection*.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no counter CSV under {dirname}")
+    kern = "gather_kernel" if path_key == "gather" else "mfma_kernel"
+    acc = {}
+    for r in rows:
+        name = r.get("Kernel_Name", "")
+        ctr = r.get("Counter_Name", "")
+        val = float(r.get("Counter_Value", "nan"))
+        key = "copy" if ("copy" in name.lower() or "elementwise" in name.lower()) else ("fwd" if kern in name else None)
+        if key is None or ctr not in ("FETCH_SIZE", "WRITE_SIZE"):
+            continue
+        acc.setdefault((key, ctr), []).append(val)
+    res = {k[0] + "_" + k[1]: float(np.mean(v)) for k, v in acc.items()}
+    copy_read = res.get("copy_FETCH_SIZE")
+    copy_write = res.get("copy_WRITE_SIZE")
+    fr = COPY_BYTES / (copy_read * 1024.0) if copy_read else None
+    fw = COPY_BYTES / (copy_write * 1024.0) if copy_write else None
+    out = {"kernel": kern, "config": config, "kernel_source_sha256_16": src_hash(path_key),
+           "fetch_kib_per_dispatch": res.get("fwd_FETCH_SIZE"), "write_kib_per_dispatch": res.get("fwd_WRITE_SIZE"),
+           "copy_fetch_kib": copy_read, "copy_write_kib": copy_write, "copy_bytes_each_way": COPY_BYTES,
+           "read_scale": fr, "write_scale": fw}
+    if res.get("fwd_FETCH_SIZE") is not None and fr and res.get("fwd_WRITE_SIZE") is not None and fw:
+        out["hbm_bytes_per_launch"] = res["fwd_FETCH_SIZE"] * 1024.0 * fr + res["fwd_WRITE_SIZE"] * 1024.0 * fw
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(counters_file(path_key, config), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); this build has no multi-GPU path. "
+              "How the work would shard over several GPUs is described in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+    import workloads as W
+    if args.ingest_counters:
+        path_key = "mfma" if args.path == "mfma" else "gather"
+        ingest_counters(args.ingest_counters, args.config, path_key)
+        return
+
+    import torch
+    import graph_sparse_attention_amd as gsa
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"# generating workload config {args.config}", file=sys.stderr, flush=True)
+    wl = W.make(args.config)
+    host = make_host_inputs(wl)
+    es = 4 if wl.dtype == "f32" else 2
+
+    if args.counters_run:
+        a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        b.copy_(a)                      # calibration: COPY_BYTES read + COPY_BYTES written
+        torch.cuda.synchronize()
+        bt = Batch(wl, dev, host)
+        rp, ci, _ = bt.csr(bt.src, bt.dst)
+        rw = gsa.gattn_build_rowwindows(rp, ci, wl.num_nodes) if args.path == "mfma" else None
+        for _ in range(5):
+            gsa.gattn_forward(rp, ci, bt.q, bt.k, bt.v, bt.e, mode=wl.mode, scale=wl.scale, clip=wl.clip,
+                              eps=wl.eps, path=args.path, rw=rw, out=bt.out)
+        torch.cuda.synchronize()
+        print("# counters run done", file=sys.stderr, flush=True)
+        return
+
+    # R rotating copies so that one step's inputs are not cache-resident
+    R = max(2, min(16, math.ceil(3 * MALL_BYTES / max(batch_bytes(wl, es), 1)) + 1))
+    print(f"# {wl.name}: N={wl.num_nodes} nnz={wl.nnz}; {R} rotating batches", file=sys.stderr, flush=True)
+    batches = [Batch(wl, dev, host) for _ in range(R)]
+    use_rw = args.path == "mfma" or (args.path == "auto" and wl.dtype != "f32" and wl.mode == "standard"
+                                     and not wl.has_e)
+
+    def step(i, ev=None):
+        b = batches[i % R]
+        if ev is not None:
+            ev[0].record()
+        rp, ci, _ = b.csr(b.src, b.dst)
+        if use_rw:
+            if b.rw is None:          # row windows once per graph (they synchronize; never inside timing)
+                b.rw = gsa.gattn_build_rowwindows(rp, ci, wl.num_nodes)
+        if ev is not None:
+            ev[1].record()
+        gsa.gattn_forward(rp, ci, b.q, b.k, b.v, b.e, mode=wl.mode, scale=wl.scale, clip=wl.clip, eps=wl.eps,
+                          path=args.path, rw=b.rw, out=b.out)
+        if ev is not None:
+            ev[2].record()
+
+    # warmup (also builds the row windows of every batch)
+    for i in range(max(args.warmup, R)):
+        step(i)
+    torch.cuda.synchronize()
+    for b in batches:
+        assert int(b.csr.status.item()) == 0, "bad graph"
+    path = gsa.gattn_forward_path(batches[0].csr.row_ptr, batches[0].csr.col_idx, batches[0].q, batches[0].k,
+                                  batches[0].v, batches[0].e, mode=wl.mode, path=args.path, rw=batches[0].rw)
+
+    # host enqueue rate, to size the sleep that keeps the GPU backlogged
+    t0 = time.perf_counter()
+    for i in range(R):
+        step(i)
+    enqueue_s = (time.perf_counter() - t0) / R
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    sleep_s = 1.5 * enqueue_s * K + 2e-3
+    torch.cuda._sleep(int(sleep_s * 2.4e9))
+    start.record()
+    for i in range(K):
+        step(i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    build_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    fwd_ms_all = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    fwd_ms = float(np.mean(fwd_ms_all))
+    ms_per_step = total_ms / K
+
+    nnz = wl.nnz
+    bmin = algorithmic_bytes(wl.num_nodes, nnz, wl.heads, wl.head_dim, es, wl.has_e)
+    achieved = bmin / (fwd_ms * 1e-3) / 1e9
+    pk = "mfma" if path == "mfma" else "gather"
+    tr = load_traffic(pk, args.config)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": (round(tr["hbm_bytes_per_launch"]) if tr and tr.get("hbm_bytes_per_launch") else None),
+                "kernel": "gather_kernel" if pk == "gather" else "mfma_kernel",
+                "algorithmic_bytes_per_launch": bmin, "bytes_per_edge": round(bmin / nnz, 2),
+                "kernel_ms": round(fwd_ms, 5), "kernel_ms_min": round(float(fwd_ms_all.min()), 5)}
+    res = {"metric": METRIC, "value": round(nnz / (ms_per_step * 1e-3) / 1e9, 4), "unit": "GEdges/s",
+           "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+           "data": "synthetic",
+           "config": {"workload": wl.name, "config_index": args.config, "nodes": wl.num_nodes, "edges": nnz,
+                      "heads": wl.heads, "head_dim": wl.head_dim, "softmax": wl.mode, "edge_projection": wl.has_e,
+                      "step": "gattn_build_csr + gattn_forward", "forward_path": path,
+                      "rotating_batches": R},
+           "roofline": roofline,
+           "forward_gedges_per_s": round(nnz / (fwd_ms * 1e-3) / 1e9, 4),
+           "build_csr_ms": round(build_ms, 5)}
+    if not args.no_cpu:
+        print("# timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,268 @@
+"""Python binding of libgattn (fused graph sparse attention, MI355X / gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libgattn.so``.  torch supplies device memory (``torch.empty``) and the
+current stream.  Names follow the C ABI in ``include/gattn.h``:
+
+    gattn_build_csr(src, dst, num_nodes)            -> (row_ptr, col_idx, edge_perm)
+    gattn_build_rowwindows(row_ptr, col_idx, n)     -> RowWindows
+    gattn_forward(row_ptr, col_idx, q, k, v, ...)   -> out [N, H, D]
+    gattn_forward_path(...)                         -> "gather" | "mfma"
+
+Importing this module raises if ``libgattn.so`` is missing: there is no
+fallback implementation.  Build it with ``python -m
+graph_sparse_attention_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Optional
+
+import torch  # loads the HIP runtime that libgattn.so then binds to
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgattn.so")
+
+GATTN_OK, GATTN_ERR_INVALID_VALUE, GATTN_ERR_UNSUPPORTED, GATTN_ERR_BAD_GRAPH, \
+    GATTN_ERR_DUPLICATE_EDGE, GATTN_ERR_BUFFER_TOO_SMALL, GATTN_ERR_HIP = range(7)
+GATTN_F32, GATTN_F16, GATTN_BF16 = range(3)
+GATTN_SOFTMAX_STANDARD, GATTN_SOFTMAX_CLIPPED = range(2)
+GATTN_PATH_AUTO, GATTN_PATH_GATHER, GATTN_PATH_MFMA = range(3)
+GATTN_FLAG_VALIDATE = 1
+
+_DTYPES = {torch.float32: GATTN_F32, torch.float16: GATTN_F16, torch.bfloat16: GATTN_BF16}
+_MODES = {"standard": GATTN_SOFTMAX_STANDARD, "clipped": GATTN_SOFTMAX_CLIPPED}
+_PATHS = {"auto": GATTN_PATH_AUTO, "gather": GATTN_PATH_GATHER, "mfma": GATTN_PATH_MFMA}
+_PATH_NAMES = {GATTN_PATH_GATHER: "gather", GATTN_PATH_MFMA: "mfma"}
+
+
+class GattnError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {gattn_status_string(status)} (status {status})")
+
+
+class _RowWindows(ctypes.Structure):
+    _fields_ = [("num_windows", ctypes.c_int32), ("num_cols", ctypes.c_int64),
+                ("win_col_ptr", ctypes.c_void_p), ("win_cols", ctypes.c_void_p), ("tile_mask", ctypes.c_void_p)]
+
+
+class _ForwardArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("num_nodes", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("nnz", ctypes.c_int64),
+                ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("e", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("dtype", ctypes.c_int), ("mode", ctypes.c_int),
+                ("scale", ctypes.c_float), ("clip_lo", ctypes.c_float), ("clip_hi", ctypes.c_float),
+                ("eps", ctypes.c_float), ("path", ctypes.c_int), ("rw", ctypes.POINTER(_RowWindows)),
+                ("flags", ctypes.c_uint32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m graph_sparse_attention_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int
+    sz = ctypes.POINTER(ctypes.c_size_t)
+    L.gattn_abi_version.restype = ctypes.c_int
+    L.gattn_status_string.argtypes = [st]
+    L.gattn_status_string.restype = ctypes.c_char_p
+    L.gattn_build_csr_workspace.argtypes = [i32, i64, sz]
+    L.gattn_build_csr.argtypes = [i32, i64, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
+    L.gattn_build_rowwindows_workspace.argtypes = [i32, i64, sz]
+    L.gattn_build_rowwindows.argtypes = [i32, i64, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_int64), vp,
+                                         ctypes.c_size_t, vp]
+    L.gattn_forward.argtypes = [ctypes.POINTER(_ForwardArgs), vp]
+    L.gattn_forward_path.argtypes = [ctypes.POINTER(_ForwardArgs), ctypes.POINTER(ctypes.c_int)]
+    for f in (L.gattn_build_csr_workspace, L.gattn_build_csr, L.gattn_build_rowwindows_workspace,
+              L.gattn_build_rowwindows, L.gattn_forward, L.gattn_forward_path):
+        f.restype = st
+    return L
+
+
+_lib = _load()
+
+
+def gattn_abi_version() -> int:
+    return _lib.gattn_abi_version()
+
+
+def gattn_status_string(status: int) -> str:
+    return _lib.gattn_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != GATTN_OK:
+        raise GattnError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor on the GPU")
+    return t
+
+
+def gattn_build_csr(src: torch.Tensor, dst: torch.Tensor, num_nodes: int, validate: bool = True):
+    """COO (src, dst) int32 on the GPU -> (row_ptr, col_idx, edge_perm),
+    canonical order (destination, source, edge id).  validate=True checks
+    indices and synchronizes; False keeps the call asynchronous (bad indices
+    then give an unspecified CSR)."""
+    src, dst = _i32(src, "src"), _i32(dst, "dst")
+    dev = src.device
+    nnz = src.numel()
+    if dst.numel() != nnz:
+        raise ValueError("src and dst differ in length")
+    nbytes = ctypes.c_size_t()
+    _check(_lib.gattn_build_csr_workspace(num_nodes, nnz, ctypes.byref(nbytes)), "gattn_build_csr_workspace")
+    ws = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
+    row_ptr = torch.empty(num_nodes + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(nnz, dtype=torch.int32, device=dev)
+    edge_perm = torch.empty(nnz, dtype=torch.int32, device=dev)
+    status = None if validate else torch.empty(1, dtype=torch.int32, device=dev)
+    _check(_lib.gattn_build_csr(num_nodes, nnz, _ptr(src), _ptr(dst), _ptr(row_ptr), _ptr(col_idx), _ptr(edge_perm),
+                                _ptr(ws), nbytes.value, _ptr(status), _stream(dev)), "gattn_build_csr")
+    return row_ptr, col_idx, edge_perm
+
+
+class CsrBuilder:
+    """Reusable buffers for repeated CSR builds of one graph size (no
+    allocation per call); the device status is kept in ``status``."""
+
+    def __init__(self, num_nodes: int, nnz: int, device):
+        self.num_nodes, self.nnz = num_nodes, nnz
+        nbytes = ctypes.c_size_t()
+        _check(_lib.gattn_build_csr_workspace(num_nodes, nnz, ctypes.byref(nbytes)), "gattn_build_csr_workspace")
+        self.ws_bytes = nbytes.value
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.row_ptr = torch.empty(num_nodes + 1, dtype=torch.int32, device=device)
+        self.col_idx = torch.empty(nnz, dtype=torch.int32, device=device)
+        self.edge_perm = torch.empty(nnz, dtype=torch.int32, device=device)
+        self.status = torch.empty(1, dtype=torch.int32, device=device)
+
+    def __call__(self, src: torch.Tensor, dst: torch.Tensor):
+        _check(_lib.gattn_build_csr(self.num_nodes, self.nnz, _ptr(src), _ptr(dst), _ptr(self.row_ptr),
+                                    _ptr(self.col_idx), _ptr(self.edge_perm), _ptr(self.ws), self.ws_bytes,
+                                    _ptr(self.status), _stream(src.device)), "gattn_build_csr")
+        return self.row_ptr, self.col_idx, self.edge_perm
+
+
+@dataclasses.dataclass
+class RowWindows:
+    num_nodes: int
+    win_col_ptr: torch.Tensor   # int32 [W+1]
+    win_cols: torch.Tensor      # int32 [C]
+    tile_mask: torch.Tensor     # int16 bits [C/16, 16] (uint16 values)
+
+    @property
+    def num_windows(self):
+        return self.win_col_ptr.numel() - 1
+
+    @property
+    def num_cols(self):
+        return self.win_cols.numel()
+
+    def _struct(self):
+        return _RowWindows(self.num_windows, self.num_cols, self.win_col_ptr.data_ptr(),
+                           self.win_cols.data_ptr() if self.num_cols else None,
+                           self.tile_mask.data_ptr() if self.num_cols else None)
+
+
+def gattn_build_rowwindows(row_ptr: torch.Tensor, col_idx: torch.Tensor, num_nodes: int) -> RowWindows:
+    """16-row windows with 16x16 masked tiles (two calls of the C ABI)."""
+    row_ptr, col_idx = _i32(row_ptr, "row_ptr"), _i32(col_idx, "col_idx")
+    dev = row_ptr.device
+    nnz = col_idx.numel()
+    nbytes = ctypes.c_size_t()
+    _check(_lib.gattn_build_rowwindows_workspace(num_nodes, nnz, ctypes.byref(nbytes)),
+           "gattn_build_rowwindows_workspace")
+    ws = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
+    W = (num_nodes + 15) // 16
+    wcp = torch.empty(W + 1, dtype=torch.int32, device=dev)
+    ncols = ctypes.c_int64(0)
+    _check(_lib.gattn_build_rowwindows(num_nodes, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(wcp), None, None,
+                                       ctypes.byref(ncols), _ptr(ws), nbytes.value, _stream(dev)),
+           "gattn_build_rowwindows (sizes)")
+    C = ncols.value
+    cols = torch.empty(max(C, 1), dtype=torch.int32, device=dev)
+    mask = torch.empty(max(C, 1), dtype=torch.int16, device=dev)
+    _check(_lib.gattn_build_rowwindows(num_nodes, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(wcp), _ptr(cols),
+                                       _ptr(mask), ctypes.byref(ncols), _ptr(ws), nbytes.value, _stream(dev)),
+           "gattn_build_rowwindows (fill)")
+    return RowWindows(num_nodes, wcp, cols[:C], mask[:C].view(C // 16, 16) if C else mask[:0].view(0, 16))
+
+
+def _forward_args(row_ptr, col_idx, q, k, v, e, out, mode, scale, clip, eps, path, rw, validate):
+    N, H, D = q.shape
+    a = _ForwardArgs()
+    a.struct_size = ctypes.sizeof(_ForwardArgs)
+    a.num_nodes, a.num_heads, a.head_dim = N, H, D
+    a.nnz = col_idx.numel()
+    a.row_ptr, a.col_idx = row_ptr.data_ptr(), col_idx.data_ptr()
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.e = None if e is None else e.data_ptr()
+    a.out = out.data_ptr() if out is not None else None
+    a.dtype = _DTYPES[q.dtype]
+    a.mode = _MODES[mode]
+    a.scale = 1.0 / math.sqrt(D) if scale is None else scale
+    a.clip_lo, a.clip_hi = clip
+    a.eps = eps
+    a.path = _PATHS[path]
+    keep = None
+    if rw is not None:
+        keep = rw._struct()
+        a.rw = ctypes.pointer(keep)
+    a.flags = GATTN_FLAG_VALIDATE if validate else 0
+    return a, keep
+
+
+def _check_node_tensor(t, name, like):
+    if t.dtype != like.dtype or t.shape != like.shape or not t.is_contiguous() or t.device != like.device:
+        raise ValueError(f"{name} must match q in dtype, shape and device and be contiguous")
+
+
+def gattn_forward(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  e: Optional[torch.Tensor] = None, mode: str = "standard", scale: Optional[float] = None,
+                  clip=(-5.0, 5.0), eps: float = 1e-6, path: str = "auto", rw: Optional[RowWindows] = None,
+                  out: Optional[torch.Tensor] = None, validate: bool = False) -> torch.Tensor:
+    """Fused SDDMM -> softmax -> SpMM over the CSR; q/k/v [N, H, D]; e
+    [nnz, H, D] by CSR position or None.  Returns out [N, H, D]."""
+    row_ptr, col_idx = _i32(row_ptr, "row_ptr"), _i32(col_idx, "col_idx")
+    if q.dim() != 3 or not q.is_contiguous() or not q.is_cuda:
+        raise ValueError("q must be a contiguous [N, H, D] GPU tensor")
+    _check_node_tensor(k, "k", q)
+    _check_node_tensor(v, "v", q)
+    N, H, D = q.shape
+    if e is not None and (e.dtype != q.dtype or tuple(e.shape) != (col_idx.numel(), H, D) or not e.is_contiguous()):
+        raise ValueError("e must be a contiguous [nnz, H, D] tensor of q's dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_node_tensor(out, "out", q)
+    a, keep = _forward_args(row_ptr, col_idx, q, k, v, e, out, mode, scale, clip, eps, path, rw, validate)
+    _check(_lib.gattn_forward(ctypes.byref(a), _stream(q.device)), "gattn_forward")
+    del keep
+    return out
+
+
+def gattn_forward_path(row_ptr, col_idx, q, k, v, e=None, mode="standard", path="auto",
+                       rw: Optional[RowWindows] = None) -> str:
+    a, keep = _forward_args(row_ptr, col_idx, q, k, v, e, None, mode, None, (-5.0, 5.0), 1e-6, path, rw, False)
+    res = ctypes.c_int(0)
+    _check(_lib.gattn_forward_path(ctypes.byref(a), ctypes.byref(res)), "gattn_forward_path")
+    del keep
+    return _PATH_NAMES[res.value]
+
+
+__all__ = ["gattn_build_csr", "gattn_build_rowwindows", "gattn_forward", "gattn_forward_path",
+           "gattn_status_string", "gattn_abi_version", "CsrBuilder", "RowWindows", "GattnError", "LIB_PATH"]

@@ -1,0 +1,224 @@
+// api.cpp -- the C ABI of libgattn: argument checks, path choice, launches.
+// Every argument error is detected here, before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "gattn.h"
+#include "internal.hpp"
+
+using namespace gattn;
+
+// the Python binding mirrors these layouts with ctypes
+static_assert(sizeof(gattn_forward_args) == 128, "gattn_forward_args layout");
+static_assert(sizeof(gattn_rowwindows) == 40, "gattn_rowwindows layout");
+
+namespace {
+
+constexpr double kMfmaMinDensity = 0.25;  // AUTO: nnz / (256 * tiles) at or above -> MFMA
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+gattn_status from_hip(hipError_t e) { return e == hipSuccess ? GATTN_OK : GATTN_ERR_HIP; }
+
+size_t elem_size(gattn_dtype t) { return t == GATTN_F32 ? 4 : 2; }
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+  if (!a || !b || an == 0 || bn == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + bn && y < x + an;
+}
+
+gattn_status check_forward(const gattn_forward_args* a, bool launch) {
+  if (!a || a->struct_size != sizeof(gattn_forward_args)) return GATTN_ERR_INVALID_VALUE;
+  if (a->num_nodes < 0 || a->num_heads < 1 || a->nnz < 0 || a->nnz > INT32_MAX) return GATTN_ERR_INVALID_VALUE;
+  if (a->dtype != GATTN_F32 && a->dtype != GATTN_F16 && a->dtype != GATTN_BF16) return GATTN_ERR_INVALID_VALUE;
+  if (a->mode != GATTN_SOFTMAX_STANDARD && a->mode != GATTN_SOFTMAX_CLIPPED) return GATTN_ERR_INVALID_VALUE;
+  if (a->path != GATTN_PATH_AUTO && a->path != GATTN_PATH_GATHER && a->path != GATTN_PATH_MFMA)
+    return GATTN_ERR_INVALID_VALUE;
+  if (a->flags & ~GATTN_FLAG_VALIDATE) return GATTN_ERR_INVALID_VALUE;
+  if (!(a->scale > 0.f) || !(a->scale < INFINITY)) return GATTN_ERR_INVALID_VALUE;
+  if (a->mode == GATTN_SOFTMAX_CLIPPED) {
+    if (!(a->clip_lo <= a->clip_hi) || !(a->eps >= 0.f) || !(a->eps < INFINITY)) return GATTN_ERR_INVALID_VALUE;
+  }
+  if (a->head_dim != 16 && a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128) return GATTN_ERR_UNSUPPORTED;
+  if ((int64_t)a->num_heads * a->head_dim > (int64_t)1 << 20) return GATTN_ERR_UNSUPPORTED;
+  if (a->num_nodes == 0) return GATTN_OK;
+  if (!a->row_ptr || !a->q || !a->k || !a->v || (launch && !a->out)) return GATTN_ERR_INVALID_VALUE;
+  if (a->nnz > 0 && !a->col_idx) return GATTN_ERR_INVALID_VALUE;
+  if (!aligned(a->row_ptr, 4) || !aligned(a->col_idx, 4)) return GATTN_ERR_INVALID_VALUE;
+  const void* t[] = {a->q, a->k, a->v, a->e, a->out};
+  for (const void* p : t)
+    if (!aligned(p, 16)) return GATTN_ERR_INVALID_VALUE;
+  const size_t node_bytes = (size_t)a->num_nodes * a->num_heads * a->head_dim * elem_size(a->dtype);
+  const size_t edge_bytes = (size_t)a->nnz * a->num_heads * a->head_dim * elem_size(a->dtype);
+  if (overlap(a->out, node_bytes, a->q, node_bytes) || overlap(a->out, node_bytes, a->k, node_bytes) ||
+      overlap(a->out, node_bytes, a->v, node_bytes) || overlap(a->out, node_bytes, a->e, edge_bytes))
+    return GATTN_ERR_INVALID_VALUE;
+  return GATTN_OK;
+}
+
+gattn_status check_rw(const gattn_forward_args* a) {
+  const gattn_rowwindows* rw = a->rw;
+  if (!rw) return GATTN_ERR_INVALID_VALUE;
+  if (rw->num_windows != (a->num_nodes + 15) / 16 || rw->num_cols < 0 || rw->num_cols % 16) return GATTN_ERR_INVALID_VALUE;
+  if (!rw->win_col_ptr || (rw->num_cols > 0 && (!rw->win_cols || !rw->tile_mask))) return GATTN_ERR_INVALID_VALUE;
+  if (!aligned(rw->win_col_ptr, 4) || !aligned(rw->win_cols, 4) || !aligned(rw->tile_mask, 4))
+    return GATTN_ERR_INVALID_VALUE;
+  return GATTN_OK;
+}
+
+gattn_status resolve(const gattn_forward_args* a, gattn_path* out) {
+  const bool mf = mfma_supported(*a);
+  if (a->path == GATTN_PATH_GATHER) { *out = GATTN_PATH_GATHER; return GATTN_OK; }
+  if (a->path == GATTN_PATH_MFMA) {
+    if (!mf) return GATTN_ERR_UNSUPPORTED;
+    gattn_status st = check_rw(a);
+    if (st != GATTN_OK) return st;
+    *out = GATTN_PATH_MFMA;
+    return GATTN_OK;
+  }
+  *out = GATTN_PATH_GATHER;
+  if (mf && a->rw && check_rw(a) == GATTN_OK && a->rw->num_cols > 0) {
+    const double density = (double)a->nnz / (16.0 * (double)a->rw->num_cols);
+    if (density >= kMfmaMinDensity) *out = GATTN_PATH_MFMA;
+  }
+  return GATTN_OK;
+}
+
+// GATTN_FLAG_VALIDATE: copy the index arrays to the host and check them
+gattn_status validate_graph(const gattn_forward_args* a, hipStream_t s) {
+  std::vector<int32_t> rp((size_t)a->num_nodes + 1), ci((size_t)a->nnz);
+  if (hipMemcpyAsync(rp.data(), a->row_ptr, rp.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess) return GATTN_ERR_HIP;
+  if (a->nnz && hipMemcpyAsync(ci.data(), a->col_idx, ci.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return GATTN_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return GATTN_ERR_HIP;
+  if (rp[0] != 0 || rp[a->num_nodes] != a->nnz) return GATTN_ERR_BAD_GRAPH;
+  for (int32_t i = 0; i < a->num_nodes; ++i)
+    if (rp[i + 1] < rp[i]) return GATTN_ERR_BAD_GRAPH;
+  for (int32_t c : ci)
+    if (c < 0 || c >= a->num_nodes) return GATTN_ERR_BAD_GRAPH;
+  return GATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gattn_abi_version(void) { return GATTN_ABI_VERSION; }
+
+const char* gattn_status_string(gattn_status s) {
+  switch (s) {
+    case GATTN_OK: return "ok";
+    case GATTN_ERR_INVALID_VALUE: return "invalid argument";
+    case GATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GATTN_ERR_BAD_GRAPH: return "malformed graph (index out of range or bad row pointer)";
+    case GATTN_ERR_DUPLICATE_EDGE: return "repeated (destination, source) pair";
+    case GATTN_ERR_BUFFER_TOO_SMALL: return "buffer or workspace too small";
+    case GATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+gattn_status gattn_build_csr_workspace(int32_t num_nodes, int64_t nnz, size_t* bytes) {
+  if (!bytes || num_nodes < 0 || nnz < 0 || nnz > INT32_MAX) return GATTN_ERR_INVALID_VALUE;
+  *bytes = build_csr_workspace_bytes(num_nodes, nnz);
+  return GATTN_OK;
+}
+
+gattn_status gattn_build_csr(int32_t num_nodes, int64_t nnz, const int32_t* src, const int32_t* dst, int32_t* row_ptr,
+                             int32_t* col_idx, int32_t* edge_perm, void* workspace, size_t workspace_bytes,
+                             int32_t* status_dev, hipStream_t stream) {
+  try {
+    if (num_nodes < 0 || nnz < 0 || nnz > INT32_MAX || !row_ptr) return GATTN_ERR_INVALID_VALUE;
+    if (nnz > 0 && (!src || !dst || !col_idx)) return GATTN_ERR_INVALID_VALUE;
+    if (!workspace || !aligned(workspace, 256)) return GATTN_ERR_INVALID_VALUE;
+    if (!aligned(src, 4) || !aligned(dst, 4) || !aligned(row_ptr, 4) || !aligned(col_idx, 4) ||
+        !aligned(edge_perm, 4) || !aligned(status_dev, 4))
+      return GATTN_ERR_INVALID_VALUE;
+    if (workspace_bytes < build_csr_workspace_bytes(num_nodes, nnz)) return GATTN_ERR_BUFFER_TOO_SMALL;
+    gattn_status st = from_hip(launch_build_csr(num_nodes, nnz, src, dst, row_ptr, col_idx, edge_perm, workspace,
+                                                status_dev, stream));
+    if (st != GATTN_OK || status_dev) return st;
+    int32_t bad = 0;
+    if (hipMemcpyAsync(&bad, workspace, sizeof(bad), hipMemcpyDeviceToHost, stream) != hipSuccess) return GATTN_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return GATTN_ERR_HIP;
+    return bad ? GATTN_ERR_BAD_GRAPH : GATTN_OK;
+  } catch (...) {
+    return GATTN_ERR_HIP;
+  }
+}
+
+gattn_status gattn_build_rowwindows_workspace(int32_t num_nodes, int64_t nnz, size_t* bytes) {
+  if (!bytes || num_nodes < 0 || nnz < 0 || nnz > INT32_MAX) return GATTN_ERR_INVALID_VALUE;
+  *bytes = rowwindows_workspace_bytes(num_nodes, nnz);
+  return GATTN_OK;
+}
+
+gattn_status gattn_build_rowwindows(int32_t num_nodes, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                                    int32_t* win_col_ptr, int32_t* win_cols, uint16_t* tile_mask, int64_t* num_cols,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  try {
+    if (num_nodes < 0 || nnz < 0 || nnz > INT32_MAX || !row_ptr || !win_col_ptr || !num_cols)
+      return GATTN_ERR_INVALID_VALUE;
+    if (nnz > 0 && !col_idx) return GATTN_ERR_INVALID_VALUE;
+    if (!workspace || !aligned(workspace, 256)) return GATTN_ERR_INVALID_VALUE;
+    if (!aligned(row_ptr, 4) || !aligned(col_idx, 4) || !aligned(win_col_ptr, 4) || !aligned(win_cols, 4) ||
+        !aligned(tile_mask, 4))
+      return GATTN_ERR_INVALID_VALUE;
+    if (workspace_bytes < rowwindows_workspace_bytes(num_nodes, nnz)) return GATTN_ERR_BUFFER_TOO_SMALL;
+    const int64_t W = (num_nodes + 15) / 16;
+    if (!win_cols) {
+      // call 1: sizes and checks; the status lives in the workspace's first 256 bytes
+      int32_t* status_dev = (int32_t*)workspace + 1;
+      hipError_t e = launch_rowwindows_count(num_nodes, nnz, row_ptr, col_idx, win_col_ptr, workspace, status_dev, stream);
+      if (e != hipSuccess) return GATTN_ERR_HIP;
+      int32_t host[2] = {0, 0};
+      if (hipMemcpyAsync(&host[0], win_col_ptr + W, 4, hipMemcpyDeviceToHost, stream) != hipSuccess) return GATTN_ERR_HIP;
+      if (hipMemcpyAsync(&host[1], status_dev, 4, hipMemcpyDeviceToHost, stream) != hipSuccess) return GATTN_ERR_HIP;
+      if (hipStreamSynchronize(stream) != hipSuccess) return GATTN_ERR_HIP;
+      if (host[1] != GATTN_OK) return (gattn_status)host[1];
+      *num_cols = host[0];
+      return GATTN_OK;
+    }
+    // call 2
+    if (!tile_mask || *num_cols < 0 || *num_cols % 16) return GATTN_ERR_INVALID_VALUE;
+    int32_t total = 0;
+    if (hipMemcpyAsync(&total, win_col_ptr + W, 4, hipMemcpyDeviceToHost, stream) != hipSuccess) return GATTN_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return GATTN_ERR_HIP;
+    if (total < 0 || total > *num_cols) return GATTN_ERR_BUFFER_TOO_SMALL;
+    return from_hip(launch_rowwindows_fill(num_nodes, nnz, row_ptr, col_idx, win_col_ptr, win_cols, tile_mask,
+                                           *num_cols, workspace, stream));
+  } catch (...) {
+    return GATTN_ERR_HIP;
+  }
+}
+
+gattn_status gattn_forward_path(const gattn_forward_args* args, gattn_path* path) {
+  if (!path) return GATTN_ERR_INVALID_VALUE;
+  gattn_status st = check_forward(args, false);
+  if (st != GATTN_OK) return st;
+  return resolve(args, path);
+}
+
+gattn_status gattn_forward(const gattn_forward_args* args, hipStream_t stream) {
+  try {
+    gattn_status st = check_forward(args, true);
+    if (st != GATTN_OK) return st;
+    gattn_path path;
+    if ((st = resolve(args, &path)) != GATTN_OK) return st;
+    if (args->num_nodes == 0) return GATTN_OK;
+    if (args->flags & GATTN_FLAG_VALIDATE) {
+      if ((st = validate_graph(args, stream)) != GATTN_OK) return st;
+    }
+    if (path == GATTN_PATH_MFMA) return from_hip(launch_forward_mfma(*args, stream));
+    return from_hip(launch_forward_gather(*args, stream));
+  } catch (...) {
+    return GATTN_ERR_HIP;
+  }
+}
+
+}  // extern "C"

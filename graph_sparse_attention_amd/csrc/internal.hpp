@@ -1,0 +1,42 @@
+// internal.hpp -- host-side launchers shared between api.cpp and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gattn.h"
+
+namespace gattn {
+
+// Exclusive prefix sum of in[0..n) into out[0..n]; out[n] = total.  in may
+// equal out.  `blocksums` needs scan_blocksums_len(n) ints.
+int64_t scan_blocksums_len(int64_t n);
+hipError_t launch_scan(const int32_t* in, int32_t* out, int64_t n, int32_t* blocksums, hipStream_t s);
+
+hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s);
+
+// CSR build ------------------------------------------------------------------
+size_t build_csr_workspace_bytes(int32_t n, int64_t nnz);
+hipError_t launch_build_csr(int32_t n, int64_t nnz, const int32_t* src, const int32_t* dst,
+                            int32_t* row_ptr, int32_t* col_idx, int32_t* edge_perm,
+                            void* ws, int32_t* status_dev, hipStream_t s);
+
+// Row windows -----------------------------------------------------------------
+size_t rowwindows_workspace_bytes(int32_t n, int64_t nnz);
+// phase 1: win_col_ptr and status (status_dev: GATTN_OK / BAD_GRAPH / DUPLICATE_EDGE)
+hipError_t launch_rowwindows_count(int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                                   int32_t* win_col_ptr, void* ws, int32_t* status_dev, hipStream_t s);
+hipError_t launch_rowwindows_fill(int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                                  const int32_t* win_col_ptr, int32_t* win_cols, uint16_t* tile_mask,
+                                  int64_t capacity, void* ws, hipStream_t s);
+
+// Forward -------------------------------------------------------------------
+hipError_t launch_forward_gather(const gattn_forward_args& a, hipStream_t s);
+hipError_t launch_forward_mfma(const gattn_forward_args& a, hipStream_t s);
+// applicability of the MFMA row-window path (no launch)
+bool mfma_supported(const gattn_forward_args& a);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace gattn

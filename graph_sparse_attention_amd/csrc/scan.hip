@@ -1,0 +1,116 @@
+// scan.hip -- exclusive prefix sum of int32 counts (reduce, scan the block
+// sums in one workgroup, scan again with offsets) and a fill kernel.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace gattn {
+
+constexpr int kScanThreads = 256;
+constexpr int kScanItems = 8;
+constexpr int kScanTile = kScanThreads * kScanItems;
+
+// inclusive scan across a 256-thread block; returns the block total in *total
+__device__ __forceinline__ int32_t block_incl_scan(int32_t x, int32_t* s_wave, int32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  int32_t off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kScanThreads / 64; ++w) {
+    const int32_t v = s_wave[w];
+    if (w < wave) off += v;
+    tot += v;
+  }
+  __syncthreads();
+  *total = tot;
+  return x + off;
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_reduce_kernel(const int32_t* __restrict__ in, int64_t n,
+                                                                   int32_t* __restrict__ blocksums) {
+  __shared__ int32_t s_wave[kScanThreads / 64];
+  const int64_t base = (int64_t)blockIdx.x * kScanTile + threadIdx.x * kScanItems;
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < kScanItems; ++i)
+    if (base + i < n) s += in[base + i];
+  int32_t total;
+  block_incl_scan(s, s_wave, &total);
+  if (threadIdx.x == 0) blocksums[blockIdx.x] = total;
+}
+
+// one workgroup: exclusive scan of blocksums[0..nb) in place, blocksums[nb] = total
+__global__ __launch_bounds__(kScanThreads) void scan_blocksums_kernel(int32_t* __restrict__ bs, int64_t nb) {
+  __shared__ int32_t s_wave[kScanThreads / 64];
+  int32_t carry = 0;
+  for (int64_t c = 0; c < nb; c += kScanTile) {
+    const int64_t base = c + threadIdx.x * kScanItems;
+    int32_t v[kScanItems], s = 0;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+      v[i] = base + i < nb ? bs[base + i] : 0;
+      s += v[i];
+    }
+    int32_t total;
+    const int32_t incl = block_incl_scan(s, s_wave, &total);
+    int32_t run = carry + incl - s;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+      if (base + i < nb) bs[base + i] = run;
+      run += v[i];
+    }
+    carry += total;
+  }
+  if (threadIdx.x == 0) bs[nb] = carry;
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(const int32_t* in, int32_t* out, int64_t n,
+                                                                  const int32_t* __restrict__ bs, int64_t nb) {
+  __shared__ int32_t s_wave[kScanThreads / 64];
+  const int64_t base = (int64_t)blockIdx.x * kScanTile + threadIdx.x * kScanItems;
+  int32_t v[kScanItems], s = 0;
+#pragma unroll
+  for (int i = 0; i < kScanItems; ++i) {
+    v[i] = base + i < n ? in[base + i] : 0;
+    s += v[i];
+  }
+  int32_t total;
+  const int32_t incl = block_incl_scan(s, s_wave, &total);
+  int32_t run = bs[blockIdx.x] + incl - s;
+#pragma unroll
+  for (int i = 0; i < kScanItems; ++i) {
+    if (base + i < n) out[base + i] = run;
+    run += v[i];
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) out[n] = bs[nb];
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int32_t value, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+int64_t scan_blocksums_len(int64_t n) { return ceil_div(std::max<int64_t>(n, 1), kScanTile) + 1; }
+
+hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>(ceil_div(n, 256), 4096);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, value, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const int32_t* in, int32_t* out, int64_t n, int32_t* blocksums, hipStream_t s) {
+  if (n == 0) return launch_fill_i32(out, 0, 1, s);
+  const int64_t nb = ceil_div(n, kScanTile);
+  hipLaunchKernelGGL(scan_reduce_kernel, dim3((unsigned)nb), dim3(kScanThreads), 0, s, in, n, blocksums);
+  hipLaunchKernelGGL(scan_blocksums_kernel, dim3(1), dim3(kScanThreads), 0, s, blocksums, nb);
+  hipLaunchKernelGGL(scan_apply_kernel, dim3((unsigned)nb), dim3(kScanThreads), 0, s, in, out, n, blocksums, nb);
+  return hipGetLastError();
+}
+
+}  // namespace gattn

@@ -1,0 +1,192 @@
+/* gattn.h -- fused graph sparse attention on AMD Instinct MI355X (gfx950).
+ *
+ * One C ABI, three operations:
+ *
+ *   gattn_build_csr        COO edge list -> destination-grouped CSR.
+ *                          The gattn-triton article ("Using the CSC index for
+ *                          fast edge lookup") groups edges by destination with
+ *                          an N+1 pointer vector, one source per edge and a map
+ *                          from grouped position to edge id; the POPCORNBENCH
+ *                          problem calls the same arrays row_ptr / col_idx.
+ *   gattn_build_rowwindows CSR -> 16-row windows of compacted columns cut into
+ *                          16x16 tiles with per-row bit masks (Fused3S,
+ *                          Figure 1: row windows compacted and stored as
+ *                          tensor-core blocks with a binary mask).
+ *   gattn_forward          fused SDDMM -> per-destination softmax -> SpMM
+ *                          (Fused3S abstract: the "3S" pattern) with no edge
+ *                          tensor written to memory; both softmax forms:
+ *                          standard max-subtracted (Fused3S abstract) and the
+ *                          RTMScore clipped form (gattn-triton article,
+ *                          "Background" and "Fusing the full graph attention").
+ *
+ * Conventions shared by every call
+ *   - An edge j -> i has source j and destination i.  The CSR groups edges by
+ *     destination: the in-edges of node i occupy positions
+ *     [row_ptr[i], row_ptr[i+1]) and col_idx[p] is the source of position p.
+ *   - Pointers are DEVICE pointers unless marked [host].  Every buffer is owned
+ *     by the caller and must stay alive until the stream has passed the call.
+ *     The library keeps no pointer after a call returns and allocates no
+ *     device memory: scratch space is the caller's `workspace`.
+ *   - All work is enqueued on `stream` (a hipStream_t; 0 = the null stream).
+ *     Calls that must report a data-dependent result to the host say so and
+ *     synchronize that stream.
+ *   - Argument errors are detected on the host and returned before anything
+ *     is enqueued.  Errors of the HIP runtime (no device, launch failure)
+ *     return GATTN_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - Integer outputs (CSR, row windows) are unique functions of the input:
+ *     identical bits on every run.  gattn_forward uses no atomics and no
+ *     cross-workgroup communication, so it too is bit-reproducible.
+ */
+#ifndef GATTN_H
+#define GATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GATTN_ABI_VERSION 1
+
+#ifndef GATTN_API
+#define GATTN_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+  GATTN_OK = 0,
+  GATTN_ERR_INVALID_VALUE = 1,    /* null required pointer, negative size, bad enum, misaligned
+                                     tensor (q/k/v/e/out need 16-byte alignment), clip_lo > clip_hi,
+                                     eps < 0, scale not > 0, struct_size mismatch                 */
+  GATTN_ERR_UNSUPPORTED = 2,      /* head_dim not in {16,32,64,128}; H*D above 2^20; MFMA path
+                                     asked for fp32, an edge tensor, the clipped softmax or
+                                     head_dim 16                                                   */
+  GATTN_ERR_BAD_GRAPH = 3,        /* an index outside [0, N); row_ptr[0] != 0, decreasing, or
+                                     row_ptr[N] != nnz                                             */
+  GATTN_ERR_DUPLICATE_EDGE = 4,   /* gattn_build_rowwindows: a (dst, src) pair repeats, which a
+                                     bit mask cannot represent                                     */
+  GATTN_ERR_BUFFER_TOO_SMALL = 5, /* workspace or output capacity below what the size query
+                                     returned                                                      */
+  GATTN_ERR_HIP = 6               /* a HIP runtime call failed                                     */
+} gattn_status;
+
+typedef enum { GATTN_F32 = 0, GATTN_F16 = 1, GATTN_BF16 = 2 } gattn_dtype;
+
+typedef enum {
+  /* alpha_p = exp(l_p - max) / sum exp(l - max); l_p = scale * sum_d q k (e).   */
+  GATTN_SOFTMAX_STANDARD = 0,
+  /* RTMScore: t_d = clamp(scale * q_d k_d, lo, hi) (* e_d); l = clamp(sum t, lo, hi);
+     s = exp(l); alpha = s / (sum s + eps).  Elementwise clamp before the edge
+     projection and a second clamp of the sum, in the order of the article's code. */
+  GATTN_SOFTMAX_CLIPPED = 1
+} gattn_mode;
+
+typedef enum { GATTN_PATH_AUTO = 0, GATTN_PATH_GATHER = 1, GATTN_PATH_MFMA = 2 } gattn_path;
+
+#define GATTN_FLAG_VALIDATE 1u /* gattn_forward: copy row_ptr / col_idx to the host and check them
+                                  first (a debugging aid; synchronizes the stream)              */
+
+/* ------------------------------------------------------------------------ */
+GATTN_API int gattn_abi_version(void);
+GATTN_API const char* gattn_status_string(gattn_status s);
+
+/* ------------------------------------------------------------------------
+ * gattn_build_csr: COO -> CSR by destination in canonical order
+ *   (destination, source, edge id), so the result is unique.
+ *
+ *   num_nodes >= 0, 0 <= nnz < 2^31.
+ *   src, dst    [nnz] int32, COO source / destination of edge e (edge id = e).
+ *   row_ptr     [num_nodes+1] int32 out.
+ *   col_idx     [nnz] int32 out: source of each CSR position.
+ *   edge_perm   [nnz] int32 out, nullable: edge id of each CSR position (use it
+ *               to bring per-edge tensors such as E into CSR order).
+ *   workspace   device scratch of at least gattn_build_csr_workspace() bytes,
+ *               256-byte aligned.
+ *   status_dev  nullable device int32.  NULL: the call synchronizes `stream` and
+ *               returns GATTN_ERR_BAD_GRAPH when any src/dst lies outside
+ *               [0, num_nodes).  Non-NULL: the call stays asynchronous and the
+ *               device writes GATTN_OK or GATTN_ERR_BAD_GRAPH there.  Outputs are
+ *               unspecified when the graph is bad.
+ * ------------------------------------------------------------------------ */
+GATTN_API gattn_status gattn_build_csr_workspace(int32_t num_nodes, int64_t nnz, size_t* bytes /*[host]*/);
+GATTN_API gattn_status gattn_build_csr(int32_t num_nodes, int64_t nnz, const int32_t* src, const int32_t* dst,
+                             int32_t* row_ptr, int32_t* col_idx, int32_t* edge_perm,
+                             void* workspace, size_t workspace_bytes, int32_t* status_dev,
+                             hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * gattn_build_rowwindows: CSR (any order inside a row) -> row windows.
+ *   Window w covers rows [16w, min(16w+16, N)).  U_w = ascending distinct
+ *   sources of those rows, padded with -1 to a multiple of 16.
+ *     win_col_ptr[w+1] = win_col_ptr[w] + 16 * ceil(|U_w| / 16)
+ *     win_cols[win_col_ptr[w] + t] = U_w[t] or -1
+ *     tile T = win_col_ptr[w]/16 + t covers columns 16t..16t+15 of window w;
+ *     tile_mask[16*T + r] bit c (LSB = column 0) is set iff row 16w+r has an
+ *     edge from U_w[16t + c].  Rows >= N and padding columns have no bits.
+ *
+ *   Two calls.  Call 1 (win_cols == NULL): fills win_col_ptr [ceil(N/16)+1],
+ *   checks the graph (BAD_GRAPH, DUPLICATE_EDGE), synchronizes `stream` and
+ *   stores the total column count in *num_cols [host].  Call 2: *num_cols [host]
+ *   holds the capacity of win_cols [num_cols] and tile_mask [num_cols] (uint16,
+ *   i.e. num_cols/16 tiles x 16 rows); it needs win_col_ptr from call 1
+ *   unchanged, returns BUFFER_TOO_SMALL when the capacity is below
+ *   win_col_ptr[W] (read back with one small synchronous copy), then
+ *   enqueues the fill.
+ *   workspace: at least gattn_build_rowwindows_workspace() bytes (256-B aligned).
+ * ------------------------------------------------------------------------ */
+GATTN_API gattn_status gattn_build_rowwindows_workspace(int32_t num_nodes, int64_t nnz, size_t* bytes /*[host]*/);
+GATTN_API gattn_status gattn_build_rowwindows(int32_t num_nodes, int64_t nnz, const int32_t* row_ptr,
+                                    const int32_t* col_idx, int32_t* win_col_ptr, int32_t* win_cols,
+                                    uint16_t* tile_mask, int64_t* num_cols /*[host]*/,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * gattn_forward
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t num_windows;         /* ceil(num_nodes / 16)                         */
+  int64_t num_cols;            /* win_col_ptr[num_windows]                     */
+  const int32_t* win_col_ptr;  /* [num_windows + 1]                            */
+  const int32_t* win_cols;     /* [num_cols]                                   */
+  const uint16_t* tile_mask;   /* [num_cols] = [num_cols/16][16]               */
+} gattn_rowwindows;
+
+typedef struct {
+  uint32_t struct_size;        /* sizeof(gattn_forward_args)                         */
+  int32_t num_nodes;           /* N >= 0                                             */
+  int32_t num_heads;           /* H >= 1                                             */
+  int32_t head_dim;            /* D in {16, 32, 64, 128}                             */
+  int64_t nnz;                 /* edges; row_ptr[N] must equal it                    */
+  const int32_t* row_ptr;      /* [N+1] CSR by destination                           */
+  const int32_t* col_idx;      /* [nnz] source per position, any order inside a row  */
+  const void* q;               /* [N, H, D] contiguous, `dtype`, 16-byte aligned     */
+  const void* k;               /* [N, H, D]                                          */
+  const void* v;               /* [N, H, D]                                          */
+  const void* e;               /* nullable; [nnz, H, D] by CSR position              */
+  void* out;                   /* [N, H, D] `dtype`; must not alias the inputs       */
+  gattn_dtype dtype;           /* of q, k, v, e and out; arithmetic is fp32          */
+  gattn_mode mode;
+  float scale;                 /* > 0; usually 1/sqrt(D)                             */
+  float clip_lo, clip_hi;      /* clipped mode (RTMScore: -5, 5)                     */
+  float eps;                   /* clipped mode denominator term, >= 0                */
+  gattn_path path;             /* AUTO picks MFMA when it applies and rw is given    */
+  const gattn_rowwindows* rw;  /* [host] struct of device arrays; MFMA path only     */
+  uint32_t flags;              /* GATTN_FLAG_*                                       */
+} gattn_forward_args;
+
+/* out[i, h, :] = sum_p alpha_p(h) v[col_idx[p], h, :] over the in-edges p of i;
+ * a node without in-edges gets exactly 0 (0 / (0 + eps) in the clipped form).
+ * Rounding: fp32 accumulation; the fp16/bf16 output is rounded to nearest even.
+ * Without GATTN_FLAG_VALIDATE the graph is not checked; indices are clamped
+ * into range so that a bad graph gives wrong numbers, never a fault.        */
+GATTN_API gattn_status gattn_forward(const gattn_forward_args* args /*[host]*/, hipStream_t stream);
+
+/* The path gattn_forward would take for these arguments (no work enqueued; `out` may be NULL). */
+GATTN_API gattn_status gattn_forward_path(const gattn_forward_args* args /*[host]*/, gattn_path* path /*[host]*/);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GATTN_H */

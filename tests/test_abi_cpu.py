@@ -1,0 +1,145 @@
+"""The C ABI without a GPU: every symbol of include/gattn.h is exported, and
+argument errors come back before anything touches the HIP runtime.  No
+compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gattn.h")
+
+
+@pytest.fixture(scope="module")
+def gsa():
+    from graph_sparse_attention_amd import build as b
+    if not os.path.exists(b.LIB):
+        b.build()
+    import graph_sparse_attention_amd as g
+    return g
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"GATTN_API\s+[\w\s\*]+?\b(gattn_\w+)\s*\(", text)
+
+
+def test_every_declared_symbol_is_exported(gsa):
+    names = declared_functions()
+    assert len(names) == 8, names
+    lib = ctypes.CDLL(gsa.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in gattn.h but not exported"
+
+
+def test_only_the_c_abi_is_exported(gsa):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", gsa.LIB_PATH], capture_output=True, text=True).stdout
+    text_syms = [l.split()[-1] for l in out.splitlines() if " T " in l]
+    assert sorted(text_syms) == sorted(declared_functions())
+
+
+def test_enums_and_strings(gsa):
+    text = open(HEADER).read()
+    for name in ["GATTN_OK", "GATTN_ERR_INVALID_VALUE", "GATTN_ERR_UNSUPPORTED", "GATTN_ERR_BAD_GRAPH",
+                 "GATTN_ERR_DUPLICATE_EDGE", "GATTN_ERR_BUFFER_TOO_SMALL", "GATTN_ERR_HIP"]:
+        m = re.search(name + r"\s*=\s*(\d+)", text)
+        assert m and int(m.group(1)) == getattr(gsa, name)
+    assert gsa.gattn_abi_version() == 1
+    assert gsa.gattn_status_string(gsa.GATTN_ERR_DUPLICATE_EDGE).startswith("repeated")
+    assert gsa.gattn_status_string(99) == "unknown status"
+    assert ctypes.sizeof(gsa._ForwardArgs) == 128
+
+
+def fake_args(gsa, **kw):
+    a = gsa._ForwardArgs()
+    a.struct_size = ctypes.sizeof(gsa._ForwardArgs)
+    a.num_nodes, a.num_heads, a.head_dim, a.nnz = 100, 8, 64, 1000
+    base = 1 << 32   # aligned, never dereferenced: only host checks run
+    a.row_ptr, a.col_idx = base, base + (1 << 20)
+    a.q, a.k, a.v, a.out = base + (2 << 20), base + (4 << 20), base + (6 << 20), base + (8 << 20)
+    a.e = None
+    a.dtype, a.mode, a.path = gsa.GATTN_F16, gsa.GATTN_SOFTMAX_STANDARD, gsa.GATTN_PATH_AUTO
+    a.scale, a.clip_lo, a.clip_hi, a.eps = 0.125, -5.0, 5.0, 1e-6
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def path_of(gsa, a):
+    r = ctypes.c_int(-1)
+    st = gsa._lib.gattn_forward_path(ctypes.byref(a), ctypes.byref(r))
+    return st, r.value
+
+
+def test_forward_argument_errors(gsa):
+    L = gsa._lib
+    cases = [
+        (dict(struct_size=12), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(num_nodes=-1), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(num_heads=0), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(head_dim=48), gsa.GATTN_ERR_UNSUPPORTED),
+        (dict(dtype=7), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(mode=5), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(path=9), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(scale=0.0), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(scale=float("nan")), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(mode=gsa.GATTN_SOFTMAX_CLIPPED, clip_lo=1.0, clip_hi=-1.0), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(mode=gsa.GATTN_SOFTMAX_CLIPPED, eps=-1.0), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(q=(1 << 32) + 8), gsa.GATTN_ERR_INVALID_VALUE),          # misaligned
+        (dict(row_ptr=None), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(out=None), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(out=(1 << 32) + (2 << 20)), gsa.GATTN_ERR_INVALID_VALUE),  # aliases q
+        (dict(flags=8), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(path=gsa.GATTN_PATH_MFMA), gsa.GATTN_ERR_INVALID_VALUE),  # no row windows
+        (dict(path=gsa.GATTN_PATH_MFMA, dtype=gsa.GATTN_F32), gsa.GATTN_ERR_UNSUPPORTED),
+        (dict(path=gsa.GATTN_PATH_MFMA, mode=gsa.GATTN_SOFTMAX_CLIPPED), gsa.GATTN_ERR_UNSUPPORTED),
+        (dict(path=gsa.GATTN_PATH_MFMA, head_dim=16), gsa.GATTN_ERR_UNSUPPORTED),
+    ]
+    for kw, want in cases:
+        a = fake_args(gsa, **kw)
+        assert L.gattn_forward(ctypes.byref(a), None) == want, kw
+    assert L.gattn_forward(None, None) == gsa.GATTN_ERR_INVALID_VALUE
+
+
+def test_path_resolution(gsa):
+    base = 1 << 32
+    rw = gsa._RowWindows(7, 16 * 20, base + (10 << 20), base + (11 << 20), base + (12 << 20))  # density 1000/(16*320)
+    a = fake_args(gsa)
+    assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_GATHER)           # no row windows
+    a.rw = ctypes.pointer(rw)
+    assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_GATHER)           # density 0.195 < 0.25
+    rw.num_cols = 16 * 10                                                     # density 0.39
+    assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_MFMA)
+    a.e = base + (14 << 20)
+    assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_GATHER)           # edge tensor: gather only
+    a.e = None
+    a.out = None                                                              # the query needs no output
+    assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_MFMA)
+    rw.num_windows = 3
+    assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_GATHER)           # inconsistent windows ignored
+    a.path = gsa.GATTN_PATH_MFMA
+    assert path_of(gsa, a)[0] == gsa.GATTN_ERR_INVALID_VALUE
+
+
+def test_build_argument_errors(gsa):
+    L = gsa._lib
+    sz = ctypes.c_size_t()
+    assert L.gattn_build_csr_workspace(10, 20, ctypes.byref(sz)) == 0 and sz.value > 0
+    assert L.gattn_build_csr_workspace(-1, 20, ctypes.byref(sz)) == gsa.GATTN_ERR_INVALID_VALUE
+    assert L.gattn_build_csr_workspace(10, 1 << 31, ctypes.byref(sz)) == gsa.GATTN_ERR_INVALID_VALUE
+    need = sz.value if L.gattn_build_csr_workspace(10, 20, ctypes.byref(sz)) == 0 else 0
+    base = 1 << 32
+    p = lambda i: ctypes.c_void_p(base + (i << 20))
+    # null row_ptr, null COO with edges, misaligned workspace, workspace too small
+    assert L.gattn_build_csr(10, 20, p(1), p(2), None, p(4), p(5), p(6), need, None, None) == 1
+    assert L.gattn_build_csr(10, 20, None, p(2), p(3), p(4), p(5), p(6), need, None, None) == 1
+    assert L.gattn_build_csr(10, 20, p(1), p(2), p(3), p(4), p(5), ctypes.c_void_p(base + 64), need, None, None) == 1
+    assert L.gattn_build_csr(10, 20, p(1), p(2), p(3), p(4), p(5), p(6), need - 1, None, None) == 5
+    assert L.gattn_build_rowwindows_workspace(10, 20, ctypes.byref(sz)) == 0
+    need = sz.value
+    nc = ctypes.c_int64(0)
+    assert L.gattn_build_rowwindows(10, 20, p(1), p(2), p(3), None, None, None, p(6), need, None) == 1
+    assert L.gattn_build_rowwindows(10, 20, None, p(2), p(3), None, None, ctypes.byref(nc), p(6), need, None) == 1
+    assert L.gattn_build_rowwindows(10, 20, p(1), p(2), p(3), None, None, ctypes.byref(nc), p(6), need - 8, None) == 5

@@ -1,0 +1,166 @@
+"""GPU: CSR and row-window construction, bit-exact against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gsa():
+    import graph_sparse_attention_amd as g
+    return g
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()
+
+
+def gpu_csr(gsa, n, src, dst):
+    s = torch.from_numpy(np.ascontiguousarray(src, np.int32)).cuda()
+    d = torch.from_numpy(np.ascontiguousarray(dst, np.int32)).cuda()
+    rp, ci, pe = gsa.gattn_build_csr(s, d, n)
+    return to_np(rp), to_np(ci), to_np(pe)
+
+
+def assert_csr_equal(gsa, n, src, dst):
+    ref = oracle.build_csr(n, src, dst)
+    got = gpu_csr(gsa, n, src, dst)
+    for name, a, b in zip(("row_ptr", "col_idx", "edge_perm"), got, ref):
+        assert np.array_equal(a, b), f"{name} differs"
+    return ref
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_csr_configs(gsa, cfg):
+    c = case(cfg)
+    got = gpu_csr(gsa, c.n, c.wl.src, c.wl.dst)
+    for a, b in zip(got, (c.rp, c.ci, c.pe)):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.slow
+def test_csr_config4(gsa):
+    c = case(4)
+    rp, ci, pe = gsa.gattn_build_csr(c.src, c.dst, c.n)
+    assert np.array_equal(to_np(rp), c.rp)
+    assert np.array_equal(to_np(ci), c.ci)
+    assert np.array_equal(to_np(pe), c.pe)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_csr_fuzz(gsa, seed):
+    n = [1, 2, 17, 64, 100, 1000, 3, 500][seed]
+    src, dst = W.random_graph(500 + seed, seed, n, [5, 70, 40, 66, 130, 20, 1, 90][seed], multi=seed % 2 == 1)
+    assert_csr_equal(gsa, n, src, dst)
+
+
+def test_csr_long_rows(gsa):
+    # one destination above the LDS sort capacity (chunks ranked by binary search),
+    # rows of exactly 64 and 65 in-edges, and isolated nodes
+    g = np.random.default_rng(3)
+    n = 30000
+    src = [g.integers(0, n, 20000), g.integers(0, n, 64), g.integers(0, n, 65), g.integers(0, n, 8192)]
+    dst = [np.full(20000, 7), np.full(64, 8), np.full(65, 9), np.full(8192, 10)]
+    src, dst = np.concatenate(src).astype(np.int32), np.concatenate(dst).astype(np.int32)
+    perm = g.permutation(src.shape[0])
+    assert_csr_equal(gsa, n, src[perm], dst[perm])
+
+
+def test_csr_empty_and_bad(gsa):
+    for n in (0, 5):
+        rp, ci, pe = gpu_csr(gsa, n, np.zeros(0, np.int32), np.zeros(0, np.int32))
+        assert rp.tolist() == [0] * (n + 1) and ci.size == 0
+    with pytest.raises(gsa.GattnError) as ei:
+        gpu_csr(gsa, 5, np.array([0, 5], np.int32), np.array([1, 2], np.int32))
+    assert ei.value.status == gsa.GATTN_ERR_BAD_GRAPH
+    # asynchronous form: status written on the device
+    b = gsa.CsrBuilder(5, 2, "cuda")
+    b(torch.tensor([0, 1], dtype=torch.int32, device="cuda"), torch.tensor([-1, 2], dtype=torch.int32, device="cuda"))
+    assert int(b.status.item()) == gsa.GATTN_ERR_BAD_GRAPH
+    b(torch.tensor([0, 1], dtype=torch.int32, device="cuda"), torch.tensor([4, 2], dtype=torch.int32, device="cuda"))
+    assert int(b.status.item()) == gsa.GATTN_OK
+    assert to_np(b.row_ptr).tolist() == [0, 0, 0, 1, 1, 2]
+
+
+def test_csr_deterministic(gsa):
+    c = case(3)
+    a = gsa.gattn_build_csr(c.src, c.dst, c.n)
+    b = gsa.gattn_build_csr(c.src, c.dst, c.n)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def gpu_rw(gsa, n, rp, ci):
+    rw = gsa.gattn_build_rowwindows(torch.from_numpy(np.ascontiguousarray(rp)).cuda(),
+                                    torch.from_numpy(np.ascontiguousarray(ci)).cuda(), n)
+    return to_np(rw.win_col_ptr), to_np(rw.win_cols), to_np(rw.tile_mask).view(np.uint16)
+
+
+def assert_rw_equal(gsa, n, rp, ci):
+    ref = oracle.rowwindows(n, rp, ci)
+    got = gpu_rw(gsa, n, rp, ci)
+    for name, a, b in zip(("win_col_ptr", "win_cols", "tile_mask"), got, ref):
+        assert np.array_equal(a, b.reshape(a.shape)), f"{name} differs"
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_rowwindows_configs(gsa, cfg):
+    c = case(cfg)
+    assert_rw_equal(gsa, c.n, c.rp, c.ci)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_rowwindows_fuzz(gsa, seed):
+    n = [1, 16, 17, 33, 250, 1000][seed]
+    src, dst = W.random_graph(600 + seed, seed, n, [3, 16, 30, 40, 25, 12][seed])
+    rp, ci, _ = oracle.build_csr(n, src, dst)
+    assert_rw_equal(gsa, n, rp, ci)
+    # any order inside a row gives the same windows
+    g = np.random.default_rng(seed)
+    ci2 = ci.copy()
+    for i in range(n):
+        g.shuffle(ci2[rp[i]:rp[i + 1]])
+    ref = oracle.rowwindows(n, rp, ci)
+    got = gpu_rw(gsa, n, rp, ci2)
+    for a, b in zip(got, ref):
+        assert np.array_equal(a, b.reshape(a.shape))
+
+
+def test_rowwindows_long_window(gsa):
+    # a window with more than 8192 edges takes the chunked workspace sort
+    n = 20000
+    g = np.random.default_rng(9)
+    srcs, dsts = [], []
+    for r in range(16, 32):
+        s = g.choice(n, 700, replace=False)
+        srcs.append(s)
+        dsts.append(np.full(700, r))
+    srcs.append(g.choice(n, 50, replace=False))
+    dsts.append(np.full(50, 40))
+    src, dst = np.concatenate(srcs).astype(np.int32), np.concatenate(dsts).astype(np.int32)
+    rp, ci, _ = oracle.build_csr(n, src, dst)
+    assert_rw_equal(gsa, n, rp, ci)
+
+
+def test_rowwindows_errors(gsa):
+    n = 40
+    src, dst = W.random_graph(700, 0, n, 10)
+    src, dst = np.append(src, src[0]).astype(np.int32), np.append(dst, dst[0]).astype(np.int32)
+    rp, ci, _ = oracle.build_csr(n, src, dst)
+    with pytest.raises(gsa.GattnError) as ei:
+        gpu_rw(gsa, n, rp, ci)
+    assert ei.value.status == gsa.GATTN_ERR_DUPLICATE_EDGE
+    ci_bad = ci.copy()
+    ci_bad[3] = n
+    with pytest.raises(gsa.GattnError) as ei:
+        gpu_rw(gsa, n, rp, ci_bad)
+    assert ei.value.status == gsa.GATTN_ERR_BAD_GRAPH
+    # empty graph
+    rp0 = np.zeros(n + 1, np.int32)
+    wcp, cols, mask = gpu_rw(gsa, n, rp0, np.zeros(0, np.int32))
+    assert np.all(wcp == 0) and cols.size == 0

@@ -1,0 +1,174 @@
+"""GPU: fused forward (gather and MFMA row-window paths) against the oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import FP32_TOL, REL_L2_TOL, TORCH_DTYPE, case, check_forward
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gsa():
+    import graph_sparse_attention_amd as g
+    return g
+
+
+def gpu_forward(gsa, c, path="gather", rw=None, rp=None, ci=None):
+    wl = c.wl
+    rp_t = torch.from_numpy(c.rp if rp is None else rp).cuda()
+    ci_t = torch.from_numpy(c.ci if ci is None else ci).cuda()
+    return gsa.gattn_forward(rp_t, ci_t, c.q, c.k, c.v, c.e, mode=wl.mode, scale=wl.scale, clip=wl.clip,
+                             eps=wl.eps, path=path, rw=rw)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_configs_gather(gsa, cfg):
+    c = case(cfg)
+    ref, mag = c.oracle_forward()
+    out = gpu_forward(gsa, c, "gather")
+    err = check_forward(out, ref, mag, c.wl.dtype)
+    print(f"config {cfg} gather: error {err:.3e}")
+
+
+def test_config5_mfma(gsa):
+    c = case(5)
+    rp, ci = torch.from_numpy(c.rp).cuda(), torch.from_numpy(c.ci).cuda()
+    rw = gsa.gattn_build_rowwindows(rp, ci, c.n)
+    assert gsa.gattn_forward_path(rp, ci, c.q, c.k, c.v, rw=rw) == "mfma"
+    ref, mag = c.oracle_forward()
+    out = gpu_forward(gsa, c, "mfma", rw=rw)
+    err = check_forward(out, ref, mag, "f16")
+    print(f"config 5 mfma: rel-L2 {err:.3e}")
+
+
+@pytest.mark.slow
+def test_config4_sampled(gsa):
+    c = case(4)
+    rp, ci, _ = gsa.gattn_build_csr(c.src, c.dst, c.n)       # the full path: device CSR, then forward
+    assert torch.equal(rp.cpu(), torch.from_numpy(c.rp)) and torch.equal(ci.cpu(), torch.from_numpy(c.ci))
+    out = gsa.gattn_forward(rp, ci, c.q, c.k, c.v, mode="standard", scale=c.wl.scale, path="gather")
+    deg = np.diff(c.rp)
+    g = np.random.default_rng(4)
+    rows = np.concatenate([g.choice(c.n, 30000, replace=False), np.argsort(deg)[-64:]]).astype(np.int32)
+    ref, mag = c.oracle_forward(rows=rows)
+    err = check_forward(out, ref, mag, "bf16", rows=rows)
+    print(f"config 4 sampled: rel-L2 {err:.3e}")
+
+
+# ---- a matrix of small random cases ------------------------------------------------
+
+def small_case(n, deg_max, h, d, dtype, mode, with_e, seed, multi=False):
+    src, dst = W.random_graph(800 + seed, seed, n, deg_max, multi=multi)
+    rp, ci, pe = oracle.build_csr(n, src, dst)
+    g = np.random.default_rng(seed)
+    mk = lambda *s: W.cast(g.standard_normal(s, dtype=np.float32) * 1.5, dtype)
+    q, k, v = mk(n, h, d), mk(n, h, d), mk(n, h, d)
+    e = mk(src.shape[0], h, d) if with_e else None
+    return rp, ci, q, k, v, e
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("mode", ["standard", "clipped"])
+@pytest.mark.parametrize("with_e", [False, True])
+@pytest.mark.parametrize("hd", [(1, 16), (3, 32), (8, 64), (2, 128), (8, 16), (5, 128)])
+def test_matrix_gather(gsa, dtype, mode, with_e, hd):
+    h, d = hd
+    seed = (h * 131 + d) % 97 + (7 if with_e else 0) + (3 if mode == "clipped" else 0)
+    n = 203
+    rp, ci, q, k, v, e = small_case(n, 40, h, d, dtype, mode, with_e, seed)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    ref, mag = oracle.forward(rp, ci, oracle.widen(q), oracle.widen(k), oracle.widen(v),
+                              None if e is None else oracle.widen(e), mode=mode, scale=scale, want_mag=True)
+    out = gsa.gattn_forward(torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda(), q.cuda(), k.cuda(), v.cuda(),
+                            None if e is None else e.cuda(), mode=mode, scale=scale, path="gather")
+    check_forward(out, ref, mag, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("hd", [(1, 32), (8, 64), (3, 128), (2, 64)])
+@pytest.mark.parametrize("n", [16, 45, 300])
+def test_matrix_mfma(gsa, dtype, hd, n):
+    h, d = hd
+    rp, ci, q, k, v, _ = small_case(n, min(n, 48), h, d, dtype, "standard", False, n + d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    ref, mag = oracle.forward(rp, ci, oracle.widen(q), oracle.widen(k), oracle.widen(v), scale=scale, want_mag=True)
+    rp_t, ci_t = torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda()
+    rw = gsa.gattn_build_rowwindows(rp_t, ci_t, n)
+    out = gsa.gattn_forward(rp_t, ci_t, q.cuda(), k.cuda(), v.cuda(), scale=scale, path="mfma", rw=rw)
+    check_forward(out, ref, mag, dtype)
+
+
+@pytest.mark.parametrize("path", ["gather", "mfma"])
+def test_hubs_and_isolated(gsa, path):
+    # destinations far above a workgroup's share (split over all slots and
+    # merged in LDS), isolated destinations, single in-edges
+    n = 6000
+    g = np.random.default_rng(11)
+    srcs, dsts = [], []
+    for hub, deg in [(5, 5000), (17, 2000), (4000, 300), (4001, 70)]:
+        srcs.append(g.choice(n, deg, replace=False))
+        dsts.append(np.full(deg, hub))
+    for i in range(100, 5000, 3):
+        srcs.append(g.choice(n, 1 + i % 9, replace=False))
+        dsts.append(np.full(1 + i % 9, i))
+    src, dst = np.concatenate(srcs).astype(np.int32), np.concatenate(dsts).astype(np.int32)
+    rp, ci, pe = oracle.build_csr(n, src, dst)
+    h, d, dtype = (1, 64, "f16") if path == "mfma" else (2, 32, "f32")
+    mk = lambda *s: W.cast(g.standard_normal(s, dtype=np.float32), dtype)
+    q, k, v = mk(n, h, d), mk(n, h, d), mk(n, h, d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    ref, mag = oracle.forward(rp, ci, oracle.widen(q), oracle.widen(k), oracle.widen(v), scale=scale, want_mag=True)
+    rp_t, ci_t = torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda()
+    rw = gsa.gattn_build_rowwindows(rp_t, ci_t, n) if path == "mfma" else None
+    out = gsa.gattn_forward(rp_t, ci_t, q.cuda(), k.cuda(), v.cuda(), scale=scale, path=path, rw=rw)
+    check_forward(out, ref, mag, dtype)
+    deg = np.diff(rp)
+    one = np.flatnonzero(deg == 1)
+    assert one.size > 0
+    # a single in-edge has weight exactly 1: the output is v of its source
+    assert torch.equal(out[torch.from_numpy(one).cuda()].cpu(), v[torch.from_numpy(ci[rp[one]]).long()])
+
+
+def test_empty_and_edge_cases(gsa):
+    for n in (0, 1, 15, 17):
+        rp = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
+        ci = torch.zeros(0, dtype=torch.int32, device="cuda")
+        q = torch.randn(n, 2, 16, device="cuda")
+        out = gsa.gattn_forward(rp, ci, q, q.clone(), q.clone(), mode="clipped", path="gather")
+        assert out.shape == q.shape and torch.all(out == 0)
+
+
+def test_deterministic(gsa):
+    c = case(2)
+    a = gpu_forward(gsa, c)
+    b = gpu_forward(gsa, c)
+    assert torch.equal(a, b)
+
+
+def test_argument_errors(gsa):
+    c = case(1)
+    rp, ci = torch.from_numpy(c.rp).cuda(), torch.from_numpy(c.ci).cuda()
+    bad = torch.empty(c.q.numel() + 4, dtype=torch.float32, device="cuda")[1:1 + c.q.numel()].view(c.q.shape)
+    with pytest.raises(gsa.GattnError) as ei:
+        gsa.gattn_forward(rp, ci, bad, c.k, c.v)
+    assert ei.value.status == gsa.GATTN_ERR_INVALID_VALUE
+    with pytest.raises(gsa.GattnError) as ei:
+        gsa.gattn_forward(rp, ci, c.q, c.k, c.v, path="mfma")      # fp32 has no MFMA path
+    assert ei.value.status == gsa.GATTN_ERR_UNSUPPORTED
+    with pytest.raises(gsa.GattnError) as ei:
+        gsa.gattn_forward(rp, ci, c.q, c.k, c.v, out=c.q)          # output aliases an input
+    assert ei.value.status == gsa.GATTN_ERR_INVALID_VALUE
+    ci_bad = ci.clone()
+    ci_bad[0] = c.n + 3
+    with pytest.raises(gsa.GattnError) as ei:
+        gsa.gattn_forward(rp, ci_bad, c.q, c.k, c.v, validate=True)
+    assert ei.value.status == gsa.GATTN_ERR_BAD_GRAPH
+    # without validation a bad index is clamped: wrong numbers, no fault
+    out = gsa.gattn_forward(rp, ci_bad, c.q, c.k, c.v)
+    torch.cuda.synchronize()
+    assert out.shape == c.q.shape
