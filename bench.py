@@ -173,7 +173,7 @@ def ingest_counters(dirname, config, path_key):
         name = r.get("Kernel_Name", "")
         ctr = r.get("Counter_Name", "")
         val = float(r.get("Counter_Value", "nan"))
-        key = "copy" if ("copy" in name.lower() or "elementwise" in name.lower()) else ("fwd" if kern in name else None)
+        key = "copy" if "copyBuffer" in name else ("fwd" if kern in name else None)
         if key is None or ctr not in ("FETCH_SIZE", "WRITE_SIZE"):
             continue
         acc.setdefault((key, ctr), []).append(val)
@@ -222,7 +222,7 @@ def main():
         b = torch.empty_like(a)
         a.fill_(1.0)
         torch.cuda.synchronize()
-        b.copy_(a)                      # calibration: COPY_BYTES read + COPY_BYTES written
+        b.copy_(a)                      # calibration: COPY_BYTES read + COPY_BYTES written (runtime copyBuffer kernel)
         torch.cuda.synchronize()
         bt = Batch(wl, dev, host)
         rp, ci, _ = bt.csr(bt.src, bt.dst)

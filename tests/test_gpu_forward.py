@@ -110,12 +110,13 @@ def test_hubs_and_isolated(gsa, path):
     n = 6000
     g = np.random.default_rng(11)
     srcs, dsts = [], []
-    for hub, deg in [(5, 5000), (17, 2000), (4000, 300), (4001, 70)]:
+    for hub, deg in [(5, 5000), (17, 2000), (5500, 300), (5501, 70)]:
         srcs.append(g.choice(n, deg, replace=False))
         dsts.append(np.full(deg, hub))
     for i in range(100, 5000, 3):
-        srcs.append(g.choice(n, 1 + i % 9, replace=False))
-        dsts.append(np.full(1 + i % 9, i))
+        deg = 1 + (i // 3) % 9
+        srcs.append(g.choice(n, deg, replace=False))
+        dsts.append(np.full(deg, i))
     src, dst = np.concatenate(srcs).astype(np.int32), np.concatenate(dsts).astype(np.int32)
     rp, ci, pe = oracle.build_csr(n, src, dst)
     h, d, dtype = (1, 64, "f16") if path == "mfma" else (2, 32, "f32")
