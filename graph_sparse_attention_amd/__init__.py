@@ -24,7 +24,7 @@ from typing import Optional
 import torch  # loads the HIP runtime that libgattn.so then binds to
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgattn.so")
+LIB_PATH = os.environ.get("GATTN_LIBRARY") or os.path.join(_HERE, "libgattn.so")
 
 GATTN_OK, GATTN_ERR_INVALID_VALUE, GATTN_ERR_UNSUPPORTED, GATTN_ERR_BAD_GRAPH, \
     GATTN_ERR_DUPLICATE_EDGE, GATTN_ERR_BUFFER_TOO_SMALL, GATTN_ERR_HIP = range(7)

@@ -143,10 +143,12 @@ gattn_status gattn_build_csr(int32_t num_nodes, int64_t nnz, const int32_t* src,
     gattn_status st = from_hip(launch_build_csr(num_nodes, nnz, src, dst, row_ptr, col_idx, edge_perm, workspace,
                                                 status_dev, stream));
     if (st != GATTN_OK || status_dev) return st;
-    int32_t bad = 0;
-    if (hipMemcpyAsync(&bad, workspace, sizeof(bad), hipMemcpyDeviceToHost, stream) != hipSuccess) return GATTN_ERR_HIP;
+    // workspace head: [0] a bad index was seen, [2] the scan's bounded wait ran out
+    int32_t flags[3] = {0, 0, 0};
+    if (hipMemcpyAsync(flags, workspace, sizeof(flags), hipMemcpyDeviceToHost, stream) != hipSuccess) return GATTN_ERR_HIP;
     if (hipStreamSynchronize(stream) != hipSuccess) return GATTN_ERR_HIP;
-    return bad ? GATTN_ERR_BAD_GRAPH : GATTN_OK;
+    if (flags[0]) return GATTN_ERR_BAD_GRAPH;
+    return flags[2] ? GATTN_ERR_HIP : GATTN_OK;
   } catch (...) {
     return GATTN_ERR_HIP;
   }

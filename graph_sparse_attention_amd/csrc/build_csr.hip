@@ -7,11 +7,12 @@
 // fix the order inside a destination; we sort it by (source, edge id), which
 // makes the result unique although the scatter below uses atomics.
 //
-// Steps: count in-degrees (atomics) and flag bad indices -> exclusive scan ->
-// scatter 64-bit keys (src << 32 | edge id) with per-destination atomic
-// cursors -> sort every destination's keys: bitonic across the lanes of one
-// wave for <= 64 keys, bitonic in LDS for <= 8192 keys, and for longer rows
-// LDS-sorted chunks ranked against each other by binary search.
+// Five launches: clear the scratch -> count in-degrees (atomics) and flag bad
+// indices -> single-pass exclusive scan -> scatter 64-bit keys (src << 32 |
+// edge id), each destination counting its in-degree back down for positions
+// -> sort every destination's keys (bitonic across the lanes of one wave, four
+// 16-key rows per wave when they fit; rows above 64 keys by the workgroup in
+// LDS, as 2048-key chunks ranked by binary search beyond that).
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -19,14 +20,17 @@ namespace gattn {
 
 namespace {
 
-constexpr int kRowCap = 8192;  // keys per LDS sort (64 KiB)
+constexpr int kRowCap = 2048;  // keys per LDS sort (16 KiB)
+
+// flag words at the head of the workspace
+enum { kBad = 0, kScanErr = 2, kTicket = 3 };
 
 struct CsrWs {
-  int32_t* flags;      // [0] bad index seen, [1] number of long rows
-  int32_t* counts;     // [n]
-  int32_t* blocksums;  // scan scratch
-  uint64_t* keys;      // [nnz]
-  int32_t* long_rows;  // [n]
+  int32_t* flags;         // [64]
+  int32_t* counts;        // [n]
+  uint64_t* tile_status;  // [scan_tiles(n)]
+  uint64_t* keys;         // [nnz]
+  int64_t clear_ints;     // flags + counts + tile_status, cleared in one launch
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -38,33 +42,41 @@ CsrWs carve(void* ws, int32_t n, int64_t nnz) {
   p += 256;
   w.counts = (int32_t*)p;
   p += align256(sizeof(int32_t) * std::max<int64_t>(n, 1));
-  w.blocksums = (int32_t*)p;
-  p += align256(sizeof(int32_t) * scan_blocksums_len(n));
+  w.tile_status = (uint64_t*)p;
+  p += align256(sizeof(uint64_t) * scan_tiles(n));
+  w.clear_ints = (p - (uint8_t*)ws) / 4;
   w.keys = (uint64_t*)p;
-  p += align256(sizeof(uint64_t) * std::max<int64_t>(nnz, 1));
-  w.long_rows = (int32_t*)p;
   return w;
 }
 
+__global__ void init_kernel(int32_t* __restrict__ p, int64_t n, int32_t* __restrict__ status_dev) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+  if (status_dev && blockIdx.x == 0 && threadIdx.x == 0) *status_dev = GATTN_OK;
+}
+
 __global__ void count_kernel(const int32_t* __restrict__ src, const int32_t* __restrict__ dst, int64_t nnz,
-                             int32_t n, int32_t* __restrict__ counts, int32_t* __restrict__ flags) {
+                             int32_t n, int32_t* __restrict__ counts, int32_t* __restrict__ flags,
+                             int32_t* __restrict__ status_dev) {
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nnz; e += (int64_t)gridDim.x * blockDim.x) {
     const int32_t s = src[e], d = dst[e];
     if ((uint32_t)s >= (uint32_t)n || (uint32_t)d >= (uint32_t)n) {
-      flags[0] = 1;
+      flags[kBad] = 1;
+      if (status_dev) *status_dev = GATTN_ERR_BAD_GRAPH;
       continue;
     }
     atomicAdd(&counts[d], 1);
   }
 }
 
+// position = row start + (remaining count - 1); counts end at zero
 __global__ void scatter_kernel(const int32_t* __restrict__ src, const int32_t* __restrict__ dst, int64_t nnz,
-                               int32_t n, const int32_t* __restrict__ row_ptr, int32_t* __restrict__ cursor,
+                               int32_t n, const int32_t* __restrict__ row_ptr, int32_t* __restrict__ counts,
                                uint64_t* __restrict__ keys) {
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nnz; e += (int64_t)gridDim.x * blockDim.x) {
     const int32_t s = src[e], d = dst[e];
     if ((uint32_t)s >= (uint32_t)n || (uint32_t)d >= (uint32_t)n) continue;
-    const int32_t p = row_ptr[d] + atomicAdd(&cursor[d], 1);
+    const int32_t p = row_ptr[d] + atomicSub(&counts[d], 1) - 1;
     keys[p] = ((uint64_t)(uint32_t)s << 32) | (uint64_t)(uint32_t)e;
   }
 }
@@ -80,25 +92,10 @@ __device__ __forceinline__ void emit(int32_t* col_idx, int32_t* edge_perm, int64
   if (edge_perm) edge_perm[p] = (int32_t)(uint32_t)key;
 }
 
-// one wave per destination; rows longer than 64 are deferred to long_rows
-__global__ __launch_bounds__(256) void sort_short_rows_kernel(int32_t n, const int32_t* __restrict__ row_ptr,
-                                                              const uint64_t* __restrict__ keys,
-                                                              int32_t* __restrict__ col_idx,
-                                                              int32_t* __restrict__ edge_perm,
-                                                              int32_t* __restrict__ flags,
-                                                              int32_t* __restrict__ long_rows) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= n) return;
-  const int32_t st = row_ptr[r], d = row_ptr[r + 1] - st;
-  if (d > 64) {
-    if (lane == 0) long_rows[atomicAdd(&flags[1], 1)] = (int32_t)r;
-    return;
-  }
-  if (d <= 0) return;
-  uint64_t key = lane < d ? keys[st + lane] : ~0ull;
-  int P = 1;
-  while (P < d) P <<= 1;
+// ascending bitonic sort of aligned groups of P lanes (P a power of two <= 64);
+// the first compare of each merge pairs mirrored positions, so every
+// comparator keeps the minimum at the lower lane
+__device__ __forceinline__ uint64_t lane_bitonic(uint64_t key, int lane, int P) {
   for (int k = 2; k <= P; k <<= 1) {
     for (int j = k >> 1; j >= 1; j >>= 1) {
       const int partner = (j == (k >> 1)) ? (lane ^ (k - 1)) : (lane ^ j);
@@ -106,11 +103,10 @@ __global__ __launch_bounds__(256) void sort_short_rows_kernel(int32_t n, const i
       key = lane < partner ? (other < key ? other : key) : (other > key ? other : key);
     }
   }
-  if (lane < d) emit(col_idx, edge_perm, st + lane, key);
+  return key;
 }
 
-// LDS bitonic sort of s[0..P), P a power of two <= kRowCap; all comparators
-// ascending (the first step of each merge compares mirrored positions)
+// LDS bitonic sort of s[0..P), P a power of two <= kRowCap
 __device__ void lds_bitonic(uint64_t* s, int P) {
   for (int k = 2; k <= P; k <<= 1) {
     for (int j = k >> 1; j >= 1; j >>= 1) {
@@ -129,16 +125,59 @@ __device__ void lds_bitonic(uint64_t* s, int P) {
   }
 }
 
-__global__ __launch_bounds__(256) void sort_long_rows_kernel(const int32_t* __restrict__ row_ptr,
-                                                             uint64_t* __restrict__ keys,
-                                                             int32_t* __restrict__ col_idx,
-                                                             int32_t* __restrict__ edge_perm,
-                                                             const int32_t* __restrict__ flags,
-                                                             const int32_t* __restrict__ long_rows) {
+// A workgroup sorts 16 destinations.  Each wave takes four: side by side in
+// 16-lane segments when all have <= 16 in-edges, else one after the other
+// across the wave (<= 64).  Longer rows are listed in LDS and sorted by the
+// whole workgroup afterwards: in LDS up to kRowCap keys, beyond that as
+// LDS-sorted chunks written back and ranked against each other.
+__global__ __launch_bounds__(256) void sort_rows_kernel(int32_t n, const int32_t* __restrict__ row_ptr,
+                                                        uint64_t* __restrict__ keys, int32_t* __restrict__ col_idx,
+                                                        int32_t* __restrict__ edge_perm) {
   __shared__ uint64_t s[kRowCap];
-  const int count = flags[1];
-  for (int li = blockIdx.x; li < count; li += gridDim.x) {
-    const int32_t r = long_rows[li];
+  __shared__ int32_t s_long[16];
+  __shared__ int32_t s_nlong;
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) s_nlong = 0;
+  __syncthreads();
+  const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4;
+  if (r0 < n) {
+    const int nr = (int)min<int64_t>(4, n - r0);
+    int st[4], d[4], dmax = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st[i] = i < nr ? row_ptr[r0 + i] : 0;
+      d[i] = i < nr ? row_ptr[r0 + i + 1] - st[i] : 0;
+      dmax = max(dmax, d[i]);
+    }
+    if (dmax <= 16) {
+      const int i = lane >> 4, t = lane & 15;
+      const int64_t p = (int64_t)st[i] + t;
+      uint64_t key = t < d[i] ? keys[p] : ~0ull;
+      key = lane_bitonic(key, lane, 16);
+      if (t < d[i]) emit(col_idx, edge_perm, p, key);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (d[i] <= 1) {
+          if (d[i] == 1 && lane == 0) emit(col_idx, edge_perm, st[i], keys[st[i]]);
+          continue;
+        }
+        if (d[i] > 64) {
+          if (lane == 0) s_long[atomicAdd(&s_nlong, 1)] = (int32_t)(r0 + i);
+          continue;
+        }
+        int P = 2;
+        while (P < d[i]) P <<= 1;
+        uint64_t key = lane < d[i] ? keys[st[i] + lane] : ~0ull;
+        key = lane_bitonic(key, lane, P);
+        if (lane < d[i]) emit(col_idx, edge_perm, st[i] + lane, key);
+      }
+    }
+  }
+  __syncthreads();
+  const int nlong = s_nlong;
+  for (int li = 0; li < nlong; ++li) {
+    const int32_t r = s_long[li];
     const int32_t st = row_ptr[r], d = row_ptr[r + 1] - st;
     const int nchunks = (d + kRowCap - 1) / kRowCap;
     for (int c = 0; c < nchunks; ++c) {
@@ -177,45 +216,30 @@ __global__ __launch_bounds__(256) void sort_long_rows_kernel(const int32_t* __re
   }
 }
 
-__global__ void write_status_kernel(const int32_t* flags, int32_t* status_dev) {
-  *status_dev = flags[0] ? GATTN_ERR_BAD_GRAPH : GATTN_OK;
-}
-
 }  // namespace
 
 size_t build_csr_workspace_bytes(int32_t n, int64_t nnz) {
-  return 256 + align256(sizeof(int32_t) * std::max<int64_t>(n, 1)) +
-         align256(sizeof(int32_t) * scan_blocksums_len(n)) + align256(sizeof(uint64_t) * std::max<int64_t>(nnz, 1)) +
-         align256(sizeof(int32_t) * std::max<int64_t>(n, 1));
+  return 256 + align256(sizeof(int32_t) * std::max<int64_t>(n, 1)) + align256(sizeof(uint64_t) * scan_tiles(n)) +
+         align256(sizeof(uint64_t) * std::max<int64_t>(nnz, 1));
 }
 
 hipError_t launch_build_csr(int32_t n, int64_t nnz, const int32_t* src, const int32_t* dst, int32_t* row_ptr,
                             int32_t* col_idx, int32_t* edge_perm, void* ws, int32_t* status_dev, hipStream_t s) {
   CsrWs w = carve(ws, n, nnz);
-  hipError_t err;
-  if ((err = launch_fill_i32(w.flags, 0, 2, s)) != hipSuccess) return err;
-  if ((err = launch_fill_i32(w.counts, 0, n, s)) != hipSuccess) return err;
+  const unsigned cblocks = (unsigned)std::min<int64_t>(ceil_div(w.clear_ints, 256), 2048);
+  hipLaunchKernelGGL(init_kernel, dim3(cblocks), dim3(256), 0, s, w.flags, w.clear_ints, status_dev);
   const unsigned eblocks = (unsigned)std::min<int64_t>(std::max<int64_t>(ceil_div(nnz, 256), 1), 16384);
-  if (nnz > 0) {
-    hipLaunchKernelGGL(count_kernel, dim3(eblocks), dim3(256), 0, s, src, dst, nnz, n, w.counts, w.flags);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
-  if ((err = launch_scan(w.counts, row_ptr, n, w.blocksums, s)) != hipSuccess) return err;
+  if (nnz > 0)
+    hipLaunchKernelGGL(count_kernel, dim3(eblocks), dim3(256), 0, s, src, dst, nnz, n, w.counts, w.flags, status_dev);
+  hipError_t err = launch_scan_lookback(w.counts, row_ptr, n, w.tile_status, &w.flags[kTicket], &w.flags[kScanErr],
+                                        status_dev, s);
+  if (err != hipSuccess) return err;
   if (nnz > 0 && n > 0) {
-    if ((err = launch_fill_i32(w.counts, 0, n, s)) != hipSuccess) return err;
     hipLaunchKernelGGL(scatter_kernel, dim3(eblocks), dim3(256), 0, s, src, dst, nnz, n, row_ptr, w.counts, w.keys);
-    hipLaunchKernelGGL(sort_short_rows_kernel, dim3((unsigned)ceil_div(n, 4)), dim3(256), 0, s, n, row_ptr,
-                       w.keys, col_idx, edge_perm, w.flags, w.long_rows);
-    const unsigned lblocks = (unsigned)std::min<int64_t>(std::max<int64_t>(nnz / 65, 1), 2048);
-    hipLaunchKernelGGL(sort_long_rows_kernel, dim3(lblocks), dim3(256), 0, s, row_ptr, w.keys, col_idx, edge_perm,
-                       w.flags, w.long_rows);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(sort_rows_kernel, dim3((unsigned)ceil_div(n, 16)), dim3(256), 0, s, n, row_ptr, w.keys, col_idx,
+                       edge_perm);
   }
-  if (status_dev) {
-    hipLaunchKernelGGL(write_status_kernel, dim3(1), dim3(1), 0, s, w.flags, status_dev);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 }  // namespace gattn

@@ -15,21 +15,43 @@
 //    over its D/VEC lanes with DPP inside a 16-lane row.
 //  * A workgroup owns a contiguous range of destinations (node-parallel as in
 //    the article's one-program-per-node kernels and Fused3S Figure 2, top) for
-//    one block of heads.  Its edges are cut into NS equal pieces; a slot
-//    takes the destinations whose first edge falls in its piece and walks
-//    their edges U at a time, keeping the online-softmax state (m, l) and the
-//    fp32 accumulator in registers.  A destination with many more edges than
-//    a piece is instead split over all slots, whose partial (m, l, acc) are
-//    merged through LDS in slot order -- deterministic, no atomics.
+//    one block of heads.  It first stages the destinations' row pointers and
+//    Q rows in LDS (one coalesced pass).  Its edges are then cut into NS equal
+//    contiguous pieces (a merge path over the CSR): each slot walks its piece
+//    U edges at a time, prefetching the next piece of column indices (and E
+//    rows) while it computes, and keeps the online-softmax state (m, l) and
+//    the fp32 accumulator in registers.  A destination that is cut by a piece
+//    boundary leaves partial (m, l, acc) records in LDS; the slot holding its
+//    last edge merges them in slot order.  Deterministic, no atomics.
 //  * Consecutive workgroups are mapped onto one XCD so that destinations of
 //    one batched graph, whose sources are nearby, share an L2.
 #include "common.hpp"
 #include "internal.hpp"
 
+#ifndef GATTN_GATHER_Q_LDS_BYTES
+#define GATTN_GATHER_Q_LDS_BYTES 12288  // Q rows staged per workgroup
+#endif
+#ifndef GATTN_GATHER_EDGES_PER_SLOT
+#define GATTN_GATHER_EDGES_PER_SLOT 3   // target edges per slot, in units of U
+#endif
+#ifndef GATTN_GATHER_U
+#define GATTN_GATHER_U 8                // edges per step without an edge tensor
+#endif
+#ifndef GATTN_GATHER_U_E
+#define GATTN_GATHER_U_E 4              // edges per step with an edge tensor
+#endif
+#ifndef GATTN_GATHER_E_STREAMING
+#define GATTN_GATHER_E_STREAMING 1      // non-temporal loads for the edge tensor
+#endif
+#ifndef GATTN_XCD_REMAP
+#define GATTN_XCD_REMAP 1
+#endif
+
 namespace gattn {
 
 constexpr int kGatherThreads = 256;
 constexpr int kMaxNodesPerWg = 1024;
+constexpr int kQLdsBytes = GATTN_GATHER_Q_LDS_BYTES;
 
 struct GatherArgs {
   const int32_t* __restrict__ row_ptr;
@@ -64,8 +86,10 @@ struct EdgeMath {
       s = group_sum<LPH>(s);
       const float lg = s * a.scale;  // log2 domain
       const float mn = fmaxf(m, lg);
-      const float corr = fast_exp2(m - mn);
-      const float p = fast_exp2(lg - mn);
+      // exp2(0) is exactly 1: keep the running max's own weight and an unchanged
+      // max's rescale exact (the hardware exp2 is a 1-ulp approximation)
+      const float corr = m == mn ? 1.f : fast_exp2(m - mn);
+      const float p = lg == mn ? 1.f : fast_exp2(lg - mn);
       l = l * corr + p;
 #pragma unroll
       for (int i = 0; i < VEC; ++i) acc[i] = acc[i] * corr + p * vf[i];
@@ -93,6 +117,23 @@ struct EdgeMath {
     for (int i = 0; i < VEC; ++i) o[i] = acc[i] * inv;
     st16(dst, Conv<T>::narrow(o));
   }
+
+  // fold partial state (m2, l2, acc2) into (m, l, acc), in that order
+  static __device__ __forceinline__ void fold(float& m, float& l, float* acc, float m2, float l2, const float* acc2) {
+    if constexpr (MODE == GATTN_SOFTMAX_STANDARD) {
+      const float mn = fmaxf(m, m2);
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      const float c1 = fast_exp2(m - mu), c2 = fast_exp2(m2 - mu);
+      l = l * c1 + l2 * c2;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] = acc[i] * c1 + acc2[i] * c2;
+      m = mn;
+    } else {
+      l += l2;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] += acc2[i];
+    }
+  }
 };
 
 template <typename T, int D, int MODE, bool HAS_E, int U>
@@ -103,11 +144,12 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
   constexpr int ESZ = sizeof(T);
 
   __shared__ int32_t s_rp[kMaxNodesPerWg + 1];
-  __shared__ int32_t s_big[kMaxNodesPerWg];
-  __shared__ int32_t s_nbig;
-  __shared__ float s_pm[kGatherThreads];
-  __shared__ float s_pl[kGatherThreads];
-  __shared__ float s_pacc[kGatherThreads * VEC];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[kQLdsBytes];
+  // partial records: [0] first destination of a piece (started in an earlier
+  // piece), [1] last destination of a piece (continues into a later one)
+  __shared__ float s_pm[2][kGatherThreads];
+  __shared__ float s_pl[2][kGatherThreads];
+  __shared__ float s_pacc[2][kGatherThreads * VEC];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = 1 << a.log2G;
@@ -115,6 +157,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
   const int NS = 4 * spw;
   const int slot = wave * spw + (lane >> a.log2G);
   const int lig = lane & (G - 1);
+  const int rec = slot * G + lig;
   const int hh = lig / LPH, dch = lig % LPH;
   const int hb = blockIdx.y;
   const int head = hb * a.HB + hh;
@@ -122,165 +165,152 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
   const int64_t rowstride = (int64_t)a.H * D;
   const int64_t eoff = (int64_t)head * D + dch * VEC;
   const int nmax = a.n - 1;
+  const int heads_here = min(a.HB, a.H - hb * a.HB);
+  const int chunks = heads_here * LPH;                 // 16-byte chunks of this head block per node
+  const int qrow = a.HB * D * ESZ;                     // LDS bytes per staged Q row
 
-  const int blk = (int)xcd_contiguous_block(blockIdx.x, gridDim.x);
+  const int blk = GATTN_XCD_REMAP ? (int)xcd_contiguous_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
   const int n0 = blk * a.npw;
   const int nn = min(a.npw, a.n - n0);
   const int nnz_i = (int)a.nnz;
 
-  // ---- phase 0: pointer range into LDS; list heavy destinations; zero isolated ones
+  // ---- phase 0: row pointers and Q rows into LDS (one coalesced pass)
   for (int t = tid; t <= nn; t += kGatherThreads) s_rp[t] = min(max(a.row_ptr[n0 + t], 0), nnz_i);
-  if (tid == 0) s_nbig = 0;
-  __syncthreads();
-  const int E0 = s_rp[0];
-  const int E1 = max(E0, s_rp[nn]);
-  const int C = (E1 - E0 + NS - 1) / NS;
-  const int big = max(2 * C, 16);
-  const int heads_here = min(a.HB, a.H - hb * a.HB);
-  const int chunks = heads_here * LPH;  // 16-byte chunks of this head block per node
   for (int t = tid; t < nn * chunks; t += kGatherThreads) {
     const int li = t / chunks, c = t - li * chunks;
-    if (s_rp[li + 1] - s_rp[li] <= 0) {
-      uint8_t* dst = a.out + ((int64_t)(n0 + li) * rowstride + (int64_t)hb * a.HB * D + c * VEC) * ESZ;
-      st16(dst, u32x4{0u, 0u, 0u, 0u});
+    *reinterpret_cast<u32x4*>(s_q + li * qrow + c * 16) =
+        ld16(a.q + ((int64_t)(n0 + li) * rowstride + (int64_t)hb * a.HB * D + c * VEC) * ESZ);
+  }
+  __syncthreads();
+  for (int t = tid; t < nn * chunks; t += kGatherThreads) {
+    const int li = t / chunks, c = t - li * chunks;
+    if (s_rp[li + 1] - s_rp[li] <= 0)
+      st16(a.out + ((int64_t)(n0 + li) * rowstride + (int64_t)hb * a.HB * D + c * VEC) * ESZ, u32x4{0u, 0u, 0u, 0u});
+  }
+
+  // ---- phase 1: equal contiguous pieces of the workgroup's edges
+  const int E0 = s_rp[0];
+  const int E1 = max(E0, s_rp[nn]);
+  const int C = max((E1 - E0 + NS - 1) / NS, 1);
+  const int ps = min(E0 + slot * C, E1);
+  const int pe = min(ps + C, E1);
+  int node = 0, nstart = 0, nend = 0;
+  bool first_rec = false;   // this slot holds a record [0]
+  int rec0_node = -1;
+  if (ps < pe) {
+    int lo = 0, hi = nn - 1;  // last local node with s_rp[node] <= ps
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_rp[mid] <= ps) lo = mid; else hi = mid - 1;
+    }
+    node = lo;
+    nstart = s_rp[node];
+    nend = s_rp[node + 1];
+    while (nend <= ps && node < nn - 1) {  // only reachable for malformed pointers
+      ++node;
+      nstart = nend;
+      nend = s_rp[node + 1];
     }
   }
-  for (int t = tid; t < nn; t += kGatherThreads)
-    if (s_rp[t + 1] - s_rp[t] > big) s_big[atomicAdd(&s_nbig, 1)] = t;
-  __syncthreads();
-
-  // ---- phase 1: each slot walks the light destinations that start in its piece
-  auto lower = [&](int target) {
-    int lo = 0, hi = nn;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (s_rp[mid] < target) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-  };
-  const int a_s = slot == 0 ? 0 : lower(E0 + slot * C);
-  const int a_e = slot == NS - 1 ? nn : lower(E0 + (slot + 1) * C);
-
-  int node = a_s - 1, pos = 0, end = 0;
-  auto advance = [&]() -> bool {
-    for (;;) {
-      ++node;
-      if (node >= a_e) return false;
-      pos = s_rp[node];
-      end = s_rp[node + 1];
-      if (end > pos && end - pos <= big) return true;
-    }
-  };
-  bool have = advance();
-  int cur = -1;
   float m = -INFINITY, l = 0.f, acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
   float qf[VEC];
-#pragma unroll
-  for (int i = 0; i < VEC; ++i) qf[i] = 0.f;
+  if (ps < pe && active) Conv<T>::widen(*reinterpret_cast<const u32x4*>(s_q + node * qrow + lig * 16), qf);
 
-  while (have) {
-    int cn[U], cp[U];
+  auto flush = [&]() {
+    const bool started_before = nstart < ps;
+    const bool continues = nend > pe;
+    if (!started_before && !continues) {
+      if (active) M::store(a, a.out + ((int64_t)(n0 + node) * rowstride + eoff) * ESZ, l, acc);
+    } else {
+      const int r = started_before ? 0 : 1;
+      s_pm[r][rec] = m;
+      s_pl[r][rec] = l;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (have) {
-        cn[u] = node;
-        cp[u] = pos;
-        if (++pos >= end) have = advance();
-      } else {
-        cn[u] = -1;
-        cp[u] = 0;
+      for (int i = 0; i < VEC; ++i) s_pacc[r][rec * VEC + i] = acc[i];
+      if (started_before) {
+        first_rec = true;
+        rec0_node = node;
       }
     }
-    u32x4 kr[U], vr[U], er[U], qr[U];
+  };
+
+  int colsN[U];
+  u32x4 eN[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int p = ps + u;
+    colsN[u] = p < pe ? a.col_idx[p] : 0;
+    eN[u] = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (HAS_E)
+      if (p < pe && active) eN[u] = GATTN_GATHER_E_STREAMING ? ld16_stream(a.e + ((int64_t)p * rowstride + eoff) * ESZ)
+                                       : ld16(a.e + ((int64_t)p * rowstride + eoff) * ESZ);
+  }
+  for (int base = ps; base < pe; base += U) {
+    int cols[U];
+    u32x4 er[U], kr[U], vr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      kr[u] = vr[u] = er[u] = qr[u] = u32x4{0u, 0u, 0u, 0u};
-      if (cn[u] >= 0 && active) {
-        const int j = min(max(a.col_idx[cp[u]], 0), nmax);
-        kr[u] = ld16(a.k + ((int64_t)j * rowstride + eoff) * ESZ);
-        vr[u] = ld16(a.v + ((int64_t)j * rowstride + eoff) * ESZ);
-        if constexpr (HAS_E) er[u] = ld16_stream(a.e + ((int64_t)cp[u] * rowstride + eoff) * ESZ);
-        if (u == 0 || cn[u] != cn[u - 1]) qr[u] = ld16(a.q + ((int64_t)(n0 + cn[u]) * rowstride + eoff) * ESZ);
+      cols[u] = min(max(colsN[u], 0), nmax);
+      er[u] = eN[u];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      kr[u] = vr[u] = u32x4{0u, 0u, 0u, 0u};
+      if (base + u < pe && active) {
+        kr[u] = ld16(a.k + ((int64_t)cols[u] * rowstride + eoff) * ESZ);
+        vr[u] = ld16(a.v + ((int64_t)cols[u] * rowstride + eoff) * ESZ);
+      }
+    }
+    // prefetch the next piece of indices (and edge rows) while this one computes
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = base + U + u;
+      if (p < pe) {
+        colsN[u] = a.col_idx[p];
+        if constexpr (HAS_E)
+          if (active) eN[u] = GATTN_GATHER_E_STREAMING ? ld16_stream(a.e + ((int64_t)p * rowstride + eoff) * ESZ)
+                                       : ld16(a.e + ((int64_t)p * rowstride + eoff) * ESZ);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (cn[u] < 0) break;
-      if (cn[u] != cur) {
-        if (cur >= 0 && active)
-          M::store(a, a.out + ((int64_t)(n0 + cur) * rowstride + eoff) * ESZ, l, acc);
-        cur = cn[u];
+      const int p = base + u;
+      if (p >= pe) break;
+      if (p >= nend) {
+        flush();
+        while (node < nn - 1) {  // next destination with edges (monotone pointers: one step + empties)
+          ++node;
+          nstart = nend;
+          nend = s_rp[node + 1];
+          if (nend > p) break;
+        }
         m = -INFINITY;
         l = 0.f;
 #pragma unroll
         for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+        if (active) Conv<T>::widen(*reinterpret_cast<const u32x4*>(s_q + node * qrow + lig * 16), qf);
       }
-      if (u == 0 || cn[u] != cn[u - 1]) Conv<T>::widen(qr[u], qf);
       M::step(a, qf, kr[u], er[u], vr[u], m, l, acc);
     }
   }
-  if (cur >= 0 && active) M::store(a, a.out + ((int64_t)(n0 + cur) * rowstride + eoff) * ESZ, l, acc);
+  if (ps < pe) flush();
+  __syncthreads();
 
-  // ---- phase 2: heavy destinations, split over all slots, merged in slot order
-  const int nbig = s_nbig;
-  for (int bi = 0; bi < nbig; ++bi) {
-    const int li = s_big[bi];
-    const int st = s_rp[li], en = s_rp[li + 1];
-    const int cb = (en - st + NS - 1) / NS;
-    const int ps = st + slot * cb, pe = min(ps + cb, en);
-    m = -INFINITY;
-    l = 0.f;
+  // ---- phase 2: the slot holding a cut destination's last edge merges its pieces
+  if (first_rec && s_rp[rec0_node + 1] <= pe) {
+    const int first_slot = min(max((s_rp[rec0_node] - E0) / C, 0), slot);
+    float mm = s_pm[1][first_slot * G + lig], ll = s_pl[1][first_slot * G + lig], aa[VEC];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-    if (active) Conv<T>::widen(ld16(a.q + ((int64_t)(n0 + li) * rowstride + eoff) * ESZ), qf);
-    for (int p = ps; p < pe; p += U) {
-      u32x4 kr[U], vr[U], er[U];
+    for (int i = 0; i < VEC; ++i) aa[i] = s_pacc[1][(first_slot * G + lig) * VEC + i];
+    for (int s = first_slot + 1; s <= slot; ++s) {
+      float a2[VEC];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        kr[u] = vr[u] = er[u] = u32x4{0u, 0u, 0u, 0u};
-        if (p + u < pe && active) {
-          const int j = min(max(a.col_idx[p + u], 0), nmax);
-          kr[u] = ld16(a.k + ((int64_t)j * rowstride + eoff) * ESZ);
-          vr[u] = ld16(a.v + ((int64_t)j * rowstride + eoff) * ESZ);
-          if constexpr (HAS_E) er[u] = ld16_stream(a.e + ((int64_t)(p + u) * rowstride + eoff) * ESZ);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (p + u >= pe) break;
-        M::step(a, qf, kr[u], er[u], vr[u], m, l, acc);
-      }
+      for (int i = 0; i < VEC; ++i) a2[i] = s_pacc[0][(s * G + lig) * VEC + i];
+      M::fold(mm, ll, aa, s_pm[0][s * G + lig], s_pl[0][s * G + lig], a2);
     }
-    s_pm[slot * G + lig] = m;
-    s_pl[slot * G + lig] = l;
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) s_pacc[(slot * G + lig) * VEC + i] = acc[i];
-    __syncthreads();
-    if (tid < G) {
-      const int hh2 = tid / LPH, dch2 = tid % LPH;
-      const int head2 = hb * a.HB + hh2;
-      if (hh2 < a.HB && head2 < a.H) {
-        float mm = -INFINITY;
-        if constexpr (MODE == GATTN_SOFTMAX_STANDARD)
-          for (int s = 0; s < NS; ++s) mm = fmaxf(mm, s_pm[s * G + tid]);
-        float L = 0.f, A[VEC];
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) A[i] = 0.f;
-        for (int s = 0; s < NS; ++s) {
-          const float ls = s_pl[s * G + tid];
-          if (ls == 0.f) continue;
-          const float f = (MODE == GATTN_SOFTMAX_STANDARD) ? fast_exp2(s_pm[s * G + tid] - mm) : 1.f;
-          L += ls * f;
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) A[i] += s_pacc[(s * G + tid) * VEC + i] * f;
-        }
-        const int64_t eoff2 = (int64_t)head2 * D + dch2 * VEC;
-        M::store(a, a.out + ((int64_t)(n0 + li) * rowstride + eoff2) * ESZ, L, A);
-      }
-    }
-    __syncthreads();
+    if (active) M::store(a, a.out + ((int64_t)(n0 + rec0_node) * rowstride + eoff) * ESZ, ll, aa);
   }
 }
 
@@ -289,10 +319,12 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
 // ---------------------------------------------------------------------------
 namespace {
 
+template <typename T, bool HAS_E>
+constexpr int unroll() { return HAS_E ? GATTN_GATHER_U_E : GATTN_GATHER_U; }
+
 template <typename T, int D, int MODE, bool HAS_E>
 hipError_t launch_typed(const GatherArgs& ga, dim3 grid, hipStream_t s) {
-  constexpr int U = (sizeof(T) == 4 || HAS_E) ? 4 : 8;
-  hipLaunchKernelGGL((gather_kernel<T, D, MODE, HAS_E, U>), grid, dim3(kGatherThreads), 0, s, ga);
+  hipLaunchKernelGGL((gather_kernel<T, D, MODE, HAS_E, unroll<T, HAS_E>()>), grid, dim3(kGatherThreads), 0, s, ga);
   return hipGetLastError();
 }
 
@@ -320,7 +352,8 @@ hipError_t launch_t(const gattn_forward_args& a, const GatherArgs& ga, dim3 grid
 
 hipError_t launch_forward_gather(const gattn_forward_args& a, hipStream_t s) {
   if (a.num_nodes == 0) return hipSuccess;
-  const int vec = a.dtype == GATTN_F32 ? 4 : 8;
+  const int esz = a.dtype == GATTN_F32 ? 4 : 2;
+  const int vec = 16 / esz;
   const int lph = a.head_dim / vec;
   const int hb = std::min(a.num_heads, 64 / lph);
   int g = 1;
@@ -328,12 +361,16 @@ hipError_t launch_forward_gather(const gattn_forward_args& a, hipStream_t s) {
   int log2g = 0;
   while ((1 << log2g) < g) ++log2g;
   const int ns = 4 * (64 / g);
-  const double avg = a.num_nodes > 0 ? (double)a.nnz / a.num_nodes : 0.0;
-  const int u = (a.dtype == GATTN_F32 || a.e) ? 4 : 8;
-  int npw = kMaxNodesPerWg;
+  const int u = a.e ? GATTN_GATHER_U_E : GATTN_GATHER_U;
+  // destinations per workgroup: about EDGES_PER_SLOT * U edges per slot, bounded
+  // by the LDS that stages their Q rows
+  const int qrow = hb * a.head_dim * esz;
+  const int npw_cap = std::max(1, std::min(kMaxNodesPerWg, kQLdsBytes / qrow));
+  const double avg = (double)a.nnz / a.num_nodes;
+  int npw = npw_cap;
   if (avg > 0) {
-    const double target = ns * std::max(2.0 * u, 2.0 * avg);
-    npw = (int)std::min<double>(kMaxNodesPerWg, std::max(1.0, std::ceil(target / avg)));
+    const double target = (double)ns * GATTN_GATHER_EDGES_PER_SLOT * u;
+    npw = (int)std::min<double>(npw_cap, std::max(1.0, std::ceil(target / avg)));
   }
 
   GatherArgs ga;

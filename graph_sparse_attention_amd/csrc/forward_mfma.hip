@@ -100,17 +100,40 @@ __global__ __launch_bounds__(kWavesPerWg * 64) void mfma_kernel(MfmaArgs a) {
 #pragma unroll
   for (int b = 0; b < NB; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t c = c0; c < c1; c += 16) {
-    const int32_t col = a.win_cols[c + r];
+  // K / V rows (and the mask) are loaded one tile ahead, column indices two
+  u32x4 kn[KS], vn[KS];
+  uint32_t bits_n = 0;
+  int32_t col_b = -1;
+  uint32_t mask_b = 0;
+  auto load_kv = [&](int32_t col, uint32_t mask) {
     const bool col_ok = (uint32_t)col < (uint32_t)a.n;
     const int64_t src_off = (int64_t)(col_ok ? col : 0) * rowstride + (int64_t)h * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      kn[s] = col_ok ? ld16(a.k + src_off + 32 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+      vn[s] = col_ok ? ld16(a.v + src_off + 32 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+    }
+    bits_n = mask >> (4 * g);
+  };
+  if (c0 < c1) load_kv(a.win_cols[c0 + r], a.tile_mask[c0 + r]);
+  if (c0 + 16 < c1) {
+    col_b = a.win_cols[c0 + 16 + r];
+    mask_b = a.tile_mask[c0 + 16 + r];
+  }
+
+  for (int64_t c = c0; c < c1; c += 16) {
     u32x4 kf[KS], vf[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      kf[s] = col_ok ? ld16(a.k + src_off + 32 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u};
-      vf[s] = col_ok ? ld16(a.v + src_off + 32 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+      kf[s] = kn[s];
+      vf[s] = vn[s];
     }
-    const uint32_t bits = (uint32_t)a.tile_mask[c + r] >> (4 * g);
+    const uint32_t bits = bits_n;
+    if (c + 16 < c1) load_kv(col_b, mask_b);
+    if (c + 32 < c1) {
+      col_b = a.win_cols[c + 32 + r];
+      mask_b = a.tile_mask[c + 32 + r];
+    }
 
     // SDDMM on the matrix cores
     f32x4 st = {0.f, 0.f, 0.f, 0.f};
@@ -129,11 +152,11 @@ __global__ __launch_bounds__(kWavesPerWg * 64) void mfma_kernel(MfmaArgs a) {
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float mn = fmaxf(m, tmax);
     const float mu = mn == -INFINITY ? 0.f : mn;
-    const float corr = fast_exp2(m - mu);
+    const float corr = m == mn ? 1.f : fast_exp2(m - mu);  // exp2(0) kept exact
     float p[4], psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = fast_exp2(x[i] - mu);
+      p[i] = x[i] == mu ? 1.f : fast_exp2(x[i] - mu);
       psum += p[i];
     }
     psum += __shfl_xor(psum, 16, 64);

@@ -16,6 +16,13 @@ hipError_t launch_scan(const int32_t* in, int32_t* out, int64_t n, int32_t* bloc
 
 hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s);
 
+// Single-pass exclusive scan (out[n] = total).  tile_status [scan_tiles(n)]
+// and *ticket must be zero on entry; a bounded wait that runs out sets
+// err[0] = 1 and, if given, *status_dev = GATTN_ERR_HIP.
+int64_t scan_tiles(int64_t n);
+hipError_t launch_scan_lookback(const int32_t* in, int32_t* out, int64_t n, uint64_t* tile_status, int32_t* ticket,
+                                int32_t* err, int32_t* status_dev, hipStream_t s);
+
 // CSR build ------------------------------------------------------------------
 size_t build_csr_workspace_bytes(int32_t n, int64_t nnz);
 hipError_t launch_build_csr(int32_t n, int64_t nnz, const int32_t* src, const int32_t* dst,

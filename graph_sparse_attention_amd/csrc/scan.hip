@@ -113,4 +113,88 @@ hipError_t launch_scan(const int32_t* in, int32_t* out, int64_t n, int32_t* bloc
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Single-pass exclusive scan with decoupled look-back.  Tiles take tickets in
+// launch order, so every tile a workgroup waits for has already started and
+// finishes without waiting on later ones.  A tile publishes its aggregate,
+// then its inclusive prefix, as one 64-bit word (flag << 32 | value).  The
+// wait is bounded: after kSpinLimit empty polls the tile reports an error
+// instead of spinning on.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr uint32_t kFlagAggregate = 1, kFlagPrefix = 2;
+constexpr int kSpinLimit = 1 << 20;
+
+__device__ __forceinline__ void publish(uint64_t* st, uint32_t flag, int32_t v) {
+  __hip_atomic_store(st, ((uint64_t)flag << 32) | (uint32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+}  // namespace
+
+__global__ __launch_bounds__(kScanThreads) void scan_lookback_kernel(const int32_t* __restrict__ in,
+                                                                     int32_t* __restrict__ out, int64_t n,
+                                                                     uint64_t* __restrict__ tile_status,
+                                                                     int32_t* __restrict__ ticket,
+                                                                     int32_t* __restrict__ err,
+                                                                     int32_t* __restrict__ status_dev) {
+  __shared__ int32_t s_wave[kScanThreads / 64];
+  __shared__ int32_t s_tile, s_prefix;
+  if (threadIdx.x == 0) s_tile = atomicAdd(ticket, 1);
+  __syncthreads();
+  const int64_t tile = s_tile;
+  const int64_t base = tile * kScanTile + threadIdx.x * kScanItems;
+  int32_t v[kScanItems], s = 0;
+#pragma unroll
+  for (int i = 0; i < kScanItems; ++i) {
+    v[i] = base + i < n ? in[base + i] : 0;
+    s += v[i];
+  }
+  int32_t total;
+  const int32_t incl = block_incl_scan(s, s_wave, &total);
+  if (threadIdx.x == 0) {
+    int32_t prefix = 0;
+    if (tile == 0) {
+      publish(&tile_status[0], kFlagPrefix, total);
+    } else {
+      publish(&tile_status[tile], kFlagAggregate, total);
+      int64_t j = tile - 1;
+      int spins = 0;
+      while (j >= 0) {
+        const uint64_t w = __hip_atomic_load(&tile_status[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t flag = (uint32_t)(w >> 32);
+        if (flag == 0) {
+          if (++spins > kSpinLimit) {
+            err[0] = 1;
+            if (status_dev) *status_dev = GATTN_ERR_HIP;
+            break;
+          }
+          continue;
+        }
+        prefix += (int32_t)(uint32_t)w;
+        if (flag == kFlagPrefix) break;
+        --j;
+      }
+      publish(&tile_status[tile], kFlagPrefix, prefix + total);
+    }
+    s_prefix = prefix;
+  }
+  __syncthreads();
+  int32_t run = s_prefix + incl - s;
+#pragma unroll
+  for (int i = 0; i < kScanItems; ++i) {
+    if (base + i < n) out[base + i] = run;
+    run += v[i];
+  }
+  if (base <= n && n <= base + kScanItems) out[n] = run;  // the thread holding the end writes the total
+}
+
+int64_t scan_tiles(int64_t n) { return ceil_div(std::max<int64_t>(n, 1), kScanTile); }
+
+hipError_t launch_scan_lookback(const int32_t* in, int32_t* out, int64_t n, uint64_t* tile_status, int32_t* ticket,
+                                int32_t* err, int32_t* status_dev, hipStream_t s) {
+  hipLaunchKernelGGL(scan_lookback_kernel, dim3((unsigned)scan_tiles(n)), dim3(kScanThreads), 0, s, in, out, n,
+                     tile_status, ticket, err, status_dev);
+  return hipGetLastError();
+}
+
 }  // namespace gattn

@@ -107,8 +107,10 @@ GATTN_API const char* gattn_status_string(gattn_status s);
  *   status_dev  nullable device int32.  NULL: the call synchronizes `stream` and
  *               returns GATTN_ERR_BAD_GRAPH when any src/dst lies outside
  *               [0, num_nodes).  Non-NULL: the call stays asynchronous and the
- *               device writes GATTN_OK or GATTN_ERR_BAD_GRAPH there.  Outputs are
- *               unspecified when the graph is bad.
+ *               device writes GATTN_OK or GATTN_ERR_BAD_GRAPH there (or
+ *               GATTN_ERR_HIP if the prefix sum's bounded wait ran out, which
+ *               only a broken device can cause).  Outputs are unspecified
+ *               unless the status is GATTN_OK.
  * ------------------------------------------------------------------------ */
 GATTN_API gattn_status gattn_build_csr_workspace(int32_t num_nodes, int64_t nnz, size_t* bytes /*[host]*/);
 GATTN_API gattn_status gattn_build_csr(int32_t num_nodes, int64_t nnz, const int32_t* src, const int32_t* dst,
