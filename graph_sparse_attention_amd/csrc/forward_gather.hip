@@ -322,29 +322,69 @@ namespace {
 template <typename T, bool HAS_E>
 constexpr int unroll() { return HAS_E ? GATTN_GATHER_U_E : GATTN_GATHER_U; }
 
+// Workgroups of one instantiation that fit on a CU at once (queried once).
 template <typename T, int D, int MODE, bool HAS_E>
-hipError_t launch_typed(const GatherArgs& ga, dim3 grid, hipStream_t s) {
+int resident_per_cu() {
+  static const int per_cu = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, gather_kernel<T, D, MODE, HAS_E, unroll<T, HAS_E>()>,
+                                                     kGatherThreads, 0) != hipSuccess)
+      b = 1;
+    return std::max(b, 1);
+  }();
+  return per_cu;
+}
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cus[dev] = c;
+  }
+  return cus[dev];
+}
+
+struct Geometry {
+  int npw_target, npw_cap, head_blocks;
+};
+
+// Destinations per workgroup: near the target, but rounded so that the grid is
+// a whole number of "rounds" of co-resident workgroups (a last, partly filled
+// round would leave most CUs idle while it runs).
+template <typename T, int D, int MODE, bool HAS_E>
+hipError_t launch_typed(GatherArgs ga, const Geometry& geo, hipStream_t s) {
+  const int64_t n = ga.n;
+  const int64_t resident = (int64_t)resident_per_cu<T, D, MODE, HAS_E>() * device_cus();
+  const double wgs = (double)ceil_div(n, geo.npw_target) * geo.head_blocks;
+  const int64_t rounds = std::max<int64_t>(1, (int64_t)std::llround(wgs / (double)resident));
+  const int64_t per_round = std::max<int64_t>(1, resident / geo.head_blocks);
+  int npw = (int)std::min<int64_t>(geo.npw_cap, std::max<int64_t>(1, ceil_div(n, rounds * per_round)));
+  ga.npw = npw;
+  dim3 grid((unsigned)ceil_div(n, npw), (unsigned)geo.head_blocks);
   hipLaunchKernelGGL((gather_kernel<T, D, MODE, HAS_E, unroll<T, HAS_E>()>), grid, dim3(kGatherThreads), 0, s, ga);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_d(const gattn_forward_args& a, const GatherArgs& ga, dim3 grid, hipStream_t s) {
+hipError_t launch_d(const gattn_forward_args& a, const GatherArgs& ga, const Geometry& geo, hipStream_t s) {
   const bool he = a.e != nullptr;
   if (a.mode == GATTN_SOFTMAX_STANDARD)
-    return he ? launch_typed<T, D, GATTN_SOFTMAX_STANDARD, true>(ga, grid, s)
-              : launch_typed<T, D, GATTN_SOFTMAX_STANDARD, false>(ga, grid, s);
-  return he ? launch_typed<T, D, GATTN_SOFTMAX_CLIPPED, true>(ga, grid, s)
-            : launch_typed<T, D, GATTN_SOFTMAX_CLIPPED, false>(ga, grid, s);
+    return he ? launch_typed<T, D, GATTN_SOFTMAX_STANDARD, true>(ga, geo, s)
+              : launch_typed<T, D, GATTN_SOFTMAX_STANDARD, false>(ga, geo, s);
+  return he ? launch_typed<T, D, GATTN_SOFTMAX_CLIPPED, true>(ga, geo, s)
+            : launch_typed<T, D, GATTN_SOFTMAX_CLIPPED, false>(ga, geo, s);
 }
 
 template <typename T>
-hipError_t launch_t(const gattn_forward_args& a, const GatherArgs& ga, dim3 grid, hipStream_t s) {
+hipError_t launch_t(const gattn_forward_args& a, const GatherArgs& ga, const Geometry& geo, hipStream_t s) {
   switch (a.head_dim) {
-    case 16: return launch_d<T, 16>(a, ga, grid, s);
-    case 32: return launch_d<T, 32>(a, ga, grid, s);
-    case 64: return launch_d<T, 64>(a, ga, grid, s);
-    default: return launch_d<T, 128>(a, ga, grid, s);
+    case 16: return launch_d<T, 16>(a, ga, geo, s);
+    case 32: return launch_d<T, 32>(a, ga, geo, s);
+    case 64: return launch_d<T, 64>(a, ga, geo, s);
+    default: return launch_d<T, 128>(a, ga, geo, s);
   }
 }
 
@@ -362,15 +402,16 @@ hipError_t launch_forward_gather(const gattn_forward_args& a, hipStream_t s) {
   while ((1 << log2g) < g) ++log2g;
   const int ns = 4 * (64 / g);
   const int u = a.e ? GATTN_GATHER_U_E : GATTN_GATHER_U;
-  // destinations per workgroup: about EDGES_PER_SLOT * U edges per slot, bounded
-  // by the LDS that stages their Q rows
+  // about EDGES_PER_SLOT * U edges per slot, bounded by the LDS that stages Q rows
   const int qrow = hb * a.head_dim * esz;
-  const int npw_cap = std::max(1, std::min(kMaxNodesPerWg, kQLdsBytes / qrow));
+  Geometry geo;
+  geo.npw_cap = std::max(1, std::min(kMaxNodesPerWg, kQLdsBytes / qrow));
+  geo.head_blocks = (int)ceil_div(a.num_heads, hb);
   const double avg = (double)a.nnz / a.num_nodes;
-  int npw = npw_cap;
+  geo.npw_target = geo.npw_cap;
   if (avg > 0) {
     const double target = (double)ns * GATTN_GATHER_EDGES_PER_SLOT * u;
-    npw = (int)std::min<double>(npw_cap, std::max(1.0, std::ceil(target / avg)));
+    geo.npw_target = (int)std::min<double>(geo.npw_cap, std::max(1.0, std::ceil(target / avg)));
   }
 
   GatherArgs ga;
@@ -386,16 +427,15 @@ hipError_t launch_forward_gather(const gattn_forward_args& a, hipStream_t s) {
   ga.H = a.num_heads;
   ga.HB = hb;
   ga.log2G = log2g;
-  ga.npw = npw;
+  ga.npw = 0;
   ga.scale = a.mode == GATTN_SOFTMAX_STANDARD ? a.scale * kLog2e : a.scale;
   ga.lo = a.clip_lo;
   ga.hi = a.clip_hi;
   ga.eps = a.eps;
-  dim3 grid((unsigned)ceil_div(a.num_nodes, npw), (unsigned)ceil_div(a.num_heads, hb));
   switch (a.dtype) {
-    case GATTN_F32: return launch_t<float>(a, ga, grid, s);
-    case GATTN_F16: return launch_t<_Float16>(a, ga, grid, s);
-    default: return launch_t<bf16_t>(a, ga, grid, s);
+    case GATTN_F32: return launch_t<float>(a, ga, geo, s);
+    case GATTN_F16: return launch_t<_Float16>(a, ga, geo, s);
+    default: return launch_t<bf16_t>(a, ga, geo, s);
   }
 }
 
