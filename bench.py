@@ -124,7 +124,7 @@ def cpu_baseline(wl, host, seconds):
                        threads=cores)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= seconds or reps >= 1000:
+        if el >= seconds or reps >= 100000:
             break
     cpu_model = "unknown"
     try:
