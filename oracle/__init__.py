@@ -52,10 +52,12 @@ def load(path: str):
     L.orc_rowwindow_sizes.argtypes = [ctypes.c_int32, i32p, i32p, i32p]
     L.orc_build_rowwindows.argtypes = [ctypes.c_int32, i32p, i32p, i32p, i32p, i32p]
     L.orc_forward.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
-                              i32p, i32p, i32p, i32p, i32p, i32p,
+                              i32p, i32p, i32p, i32p, i32p, i32p, i32p,
                               ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_double,
-                              ctypes.c_double, i32p, ctypes.c_int64, i32p, i32p, i32p, ctypes.c_int]
-    for f in (L.orc_build_csr, L.orc_rowwindow_sizes, L.orc_build_rowwindows, L.orc_forward):
+                              ctypes.c_double, i32p, ctypes.c_int64, i32p, i32p, i32p, i32p, ctypes.c_int]
+    L.orc_aggregate.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                i32p, i32p, i32p, i32p, i32p, ctypes.c_int, ctypes.c_double, i32p, ctypes.c_int]
+    for f in (L.orc_build_csr, L.orc_rowwindow_sizes, L.orc_build_rowwindows, L.orc_forward, L.orc_aggregate):
         f.restype = ctypes.c_int
     return L
 
@@ -133,9 +135,11 @@ def rowwindows(n: int, row_ptr, col_idx):
 
 
 def forward(row_ptr, col_idx, q, k, v, e=None, mode="standard", scale=None, clip=(-5.0, 5.0),
-            eps=1e-6, rows=None, want_mag=False, want_alpha=False, threads=1):
+            eps=1e-6, rows=None, want_mag=False, want_alpha=False, threads=1, edge_ids=None,
+            want_e_out=False):
     """fp64 fused 3S forward.  q/k/v: float64 [N,H,D]; e: float64 [nnz,H,D]
-    or None.  Returns out [nrows,H,D] (and mag, alpha when asked)."""
+    or None, row edge_ids[p] for CSR position p (row p without edge_ids).
+    Returns out [nrows,H,D] (and mag, alpha, e_out when asked)."""
     row_ptr, col_idx = _i32(row_ptr), _i32(col_idx)
     q, k, v = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v))
     n, h, d = q.shape
@@ -153,13 +157,35 @@ def forward(row_ptr, col_idx, q, k, v, e=None, mode="standard", scale=None, clip
     out = np.empty((nrows, h, d), np.float64)
     mag = np.empty((nrows, h, d), np.float64) if want_mag else None
     alpha = np.full((nnz, h), np.nan, np.float64) if want_alpha else None
+    e_out = np.full((nnz, h, d), np.nan, np.float64) if want_e_out else None
+    if edge_ids is not None:
+        edge_ids = _i32(edge_ids)
     clipped = {"standard": 0, "clipped": 1}[mode]
     _check(lib().orc_forward(n, h, d, nnz, _p(row_ptr), _p(col_idx), _p(q), _p(k), _p(v), _p(e),
-                             clipped, float(scale), float(clip[0]), float(clip[1]), float(eps),
-                             _p(rows), nrows, _p(out), _p(mag), _p(alpha), int(threads)))
+                             _p(edge_ids), clipped, float(scale), float(clip[0]), float(clip[1]), float(eps),
+                             _p(rows), nrows, _p(out), _p(mag), _p(alpha), _p(e_out), int(threads)))
     res = [out]
     if want_mag:
         res.append(mag)
     if want_alpha:
         res.append(alpha)
+    if want_e_out:
+        res.append(e_out)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def aggregate(row_ptr, col_idx, x, w, normalize=False, eps=1e-6, edge_ids=None, threads=1):
+    """fp64 weighted aggregation: x float64 [N,H,D], w float64 [nnz,H]
+    (row edge_ids[p] for CSR position p).  Returns out [N,H,D]."""
+    row_ptr, col_idx = _i32(row_ptr), _i32(col_idx)
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    n, h, d = x.shape
+    nnz = int(col_idx.shape[0])
+    assert w.shape == (nnz, h)
+    if edge_ids is not None:
+        edge_ids = _i32(edge_ids)
+    out = np.empty((n, h, d), np.float64)
+    _check(lib().orc_aggregate(n, h, d, nnz, _p(row_ptr), _p(col_idx), _p(x), _p(w), _p(edge_ids),
+                               int(bool(normalize)), float(eps), _p(out), int(threads)))
+    return out

@@ -182,8 +182,9 @@ static double clampd(double x, double lo, double hi) { return x < lo ? lo : (x >
  * the POPCORNBENCH CSR aggregation; 0/(0+eps) in the clipped form). */
 static void one_slice(int32_t i, int32_t hh, int32_t h, int32_t d, const int32_t* row_ptr,
                       const int32_t* col_idx, const double* q, const double* k, const double* v,
-                      const double* e, int clipped, double scale, double lo, double hi,
-                      double eps, double* o, double* mg, double* alpha, double* logit) {
+                      const double* e, const int32_t* edge_ids, int clipped, double scale, double lo,
+                      double hi, double eps, double* o, double* mg, double* alpha, double* e_out,
+                      double* logit) {
   int32_t b = row_ptr[i], deg = row_ptr[i + 1] - b;
   for (int32_t c = 0; c < d; ++c) { o[c] = 0.0; if (mg) mg[c] = 0.0; }
   if (deg == 0) return;
@@ -191,7 +192,8 @@ static void one_slice(int32_t i, int32_t hh, int32_t h, int32_t d, const int32_t
   for (int32_t t = 0; t < deg; ++t) {
     int64_t p = b + t;
     const double* kj = k + ((int64_t)col_idx[p] * h + hh) * d;
-    const double* ep = e ? e + (p * h + hh) * d : NULL;
+    const int64_t row = edge_ids ? (int64_t)edge_ids[p] : p;
+    const double* ep = e ? e + (row * h + hh) * d : NULL;
     double s = 0.0;
     if (!clipped) {
       for (int32_t c = 0; c < d; ++c) s += qi[c] * kj[c] * (ep ? ep[c] : 1.0);
@@ -199,7 +201,9 @@ static void one_slice(int32_t i, int32_t hh, int32_t h, int32_t d, const int32_t
     } else {
       for (int32_t c = 0; c < d; ++c) {
         double x = clampd(scale * qi[c] * kj[c], lo, hi);
-        s += ep ? x * ep[c] : x;
+        if (ep) x *= ep[c];
+        if (e_out) e_out[(row * h + hh) * d + c] = x;   /* the edge update before the sum */
+        s += x;
       }
       logit[t] = clampd(s, lo, hi);
     }
@@ -226,10 +230,14 @@ static void one_slice(int32_t i, int32_t hh, int32_t h, int32_t d, const int32_t
 int orc_forward(int32_t n, int32_t h, int32_t d, int64_t nnz,
                 const int32_t* row_ptr, const int32_t* col_idx,
                 const double* q, const double* k, const double* v, const double* e,
+                const int32_t* edge_ids,
                 int clipped, double scale, double lo, double hi, double eps,
                 const int32_t* rows, int64_t nrows,
-                double* out, double* mag, double* alpha, int threads) {
+                double* out, double* mag, double* alpha, double* e_out, int threads) {
   if (n < 0 || h < 1 || d < 1 || nnz < 0 || !row_ptr || !out || nrows < 0) return ORC_INVALID;
+  if (e_out && (!clipped || !e)) return ORC_INVALID;
+  for (int64_t p = 0; edge_ids && p < nnz; ++p)
+    if (edge_ids[p] < 0 || edge_ids[p] >= nnz) return ORC_INVALID;
   if (n > 0 && (!q || !k || !v)) return ORC_INVALID;
   if (row_ptr[n] != nnz) return ORC_BAD_GRAPH;
   int rc = check_csr(n, row_ptr, col_idx);
@@ -260,10 +268,49 @@ int orc_forward(int32_t n, int32_t h, int32_t d, int64_t nnz,
       if (!logit) continue;
       int32_t i = rows ? rows[r] : (int32_t)r;
       for (int32_t hh = 0; hh < h; ++hh)
-        one_slice(i, hh, h, d, row_ptr, col_idx, q, k, v, e, clipped, scale, lo, hi, eps,
-                  out + (r * h + hh) * d, mag ? mag + (r * h + hh) * d : NULL, alpha, logit);
+        one_slice(i, hh, h, d, row_ptr, col_idx, q, k, v, e, edge_ids, clipped, scale, lo, hi, eps,
+                  out + (r * h + hh) * d, mag ? mag + (r * h + hh) * d : NULL, alpha, e_out, logit);
     }
     free(logit);
   }
   return failed ? ORC_NOMEM : ORC_OK;
+}
+
+/* Weighted aggregation over the in-edges of each destination: the
+ * POPCORNBENCH CSR problem (out[dst] = sum of w * node features of the
+ * sources, zero for no in-edges) and, with normalize, the gattn-triton
+ * article's scatter add of value vectors and scores followed by
+ * numerator / (denominator + epsilon). */
+int orc_aggregate(int32_t n, int32_t h, int32_t d, int64_t nnz,
+                  const int32_t* row_ptr, const int32_t* col_idx,
+                  const double* x, const double* w, const int32_t* edge_ids,
+                  int normalize, double eps, double* out, int threads) {
+  if (n < 0 || h < 1 || d < 1 || nnz < 0 || !row_ptr || !out) return ORC_INVALID;
+  if (n > 0 && (!x || (nnz > 0 && !w))) return ORC_INVALID;
+  if (row_ptr[n] != nnz) return ORC_BAD_GRAPH;
+  int rc = check_csr(n, row_ptr, col_idx);
+  if (rc) return rc;
+  for (int64_t p = 0; edge_ids && p < nnz; ++p)
+    if (edge_ids[p] < 0 || edge_ids[p] >= nnz) return ORC_INVALID;
+#ifdef _OPENMP
+  if (threads < 1) threads = 1;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(threads)
+#endif
+  for (int32_t i = 0; i < n; ++i) {
+    for (int32_t hh = 0; hh < h; ++hh) {
+      double* o = out + ((int64_t)i * h + hh) * d;
+      double z = 0.0;
+      for (int32_t c = 0; c < d; ++c) o[c] = 0.0;
+      for (int32_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) {
+        const int64_t wrow = edge_ids ? (int64_t)edge_ids[p] : p;
+        const double wp = w[wrow * h + hh];
+        const double* xj = x + ((int64_t)col_idx[p] * h + hh) * d;
+        for (int32_t c = 0; c < d; ++c) o[c] += wp * xj[c];
+        z += wp;
+      }
+      if (normalize && row_ptr[i + 1] > row_ptr[i])
+        for (int32_t c = 0; c < d; ++c) o[c] /= (z + eps);
+    }
+  }
+  return ORC_OK;
 }

@@ -43,19 +43,31 @@ int orc_rowwindow_sizes(int32_t n, const int32_t* row_ptr, const int32_t* col_id
 int orc_build_rowwindows(int32_t n, const int32_t* row_ptr, const int32_t* col_idx,
                          const int32_t* win_col_ptr, int32_t* win_cols, uint16_t* tile_mask);
 
-/* Fused 3S forward, fp64.  q, k, v: [n, h, d]; e: [nnz, h, d] by CSR
- * position or NULL.  clipped = 0: standard softmax; 1: RTMScore clipped
- * exp normalised by (sum + eps).  rows: destinations to compute (NULL = all
- * n, in order); out / mag: [nrows, h, d]; mag = sum_p alpha_p |v_p|
- * (nullable); alpha: [nnz, h] by CSR position (nullable; only positions of
- * computed rows are written).  threads: OpenMP threads over destinations
- * (results do not depend on it). */
+/* Fused 3S forward, fp64.  q, k, v: [n, h, d]; e: [nnz, h, d] or NULL,
+ * row edge_ids[p] for CSR position p (edge_ids NULL: row p).  clipped = 0:
+ * standard softmax; 1: RTMScore clipped exp normalised by (sum + eps).
+ * rows: destinations to compute (NULL = all n, in order); out / mag:
+ * [nrows, h, d]; mag = sum_p alpha_p |v_p| (nullable); alpha: [nnz, h] by
+ * CSR position (nullable; only positions of computed rows are written);
+ * e_out: [nnz, h, d] (nullable, clipped mode with e only), the RTMScore
+ * edge update clamp(scale q k) e, stored at the same row as e.  threads:
+ * OpenMP threads over destinations (results do not depend on it). */
 int orc_forward(int32_t n, int32_t h, int32_t d, int64_t nnz,
                 const int32_t* row_ptr, const int32_t* col_idx,
                 const double* q, const double* k, const double* v, const double* e,
+                const int32_t* edge_ids,
                 int clipped, double scale, double lo, double hi, double eps,
                 const int32_t* rows, int64_t nrows,
-                double* out, double* mag, double* alpha, int threads);
+                double* out, double* mag, double* alpha, double* e_out, int threads);
+
+/* Weighted aggregation (the POPCORNBENCH CSR problem; with normalize = 1 the
+ * gattn-triton article's scatter add divided by the summed scores + eps):
+ * out[i, h, :] = sum_p w[id(p), h] x[col_idx[p], h, :]  (/ (sum_p w + eps)),
+ * id(p) = edge_ids ? edge_ids[p] : p.  x: [n, h, d]; w: [nnz, h]. */
+int orc_aggregate(int32_t n, int32_t h, int32_t d, int64_t nnz,
+                  const int32_t* row_ptr, const int32_t* col_idx,
+                  const double* x, const double* w, const int32_t* edge_ids,
+                  int normalize, double eps, double* out, int threads);
 
 #ifdef __cplusplus
 }

@@ -293,3 +293,65 @@ def test_rows_subset_and_threads(orc):
     rows = np.array([5, 0, 319, 5], np.int32)
     sub = orc.forward(rp, ci, q, k, v, scale=wl.scale, rows=rows)
     assert np.array_equal(sub, full[rows])
+
+
+# ---- edge update output, edge-id indirection, weighted aggregation ---------------
+
+def test_e_out_is_the_elementwise_update(orc):
+    """The edge update (the article's per-edge store before the feature sum)
+    restated as a vectorised edge-list expression."""
+    n, h, d = 50, 3, 8
+    src, dst = W.random_graph(910, 1, n, 12)
+    q, k, v, e = feats(21, n, src.shape[0], h, d, True)
+    q *= 3.0
+    scale = 0.3
+    rp, ci, pe = orc.build_csr(n, src, dst)
+    out, e_out = orc.forward(rp, ci, q, k, v, e, mode="clipped", scale=scale, edge_ids=pe, want_e_out=True)
+    ref = np.clip(scale * q[dst] * k[src], -5.0, 5.0) * e            # rows in the caller's edge order
+    np.testing.assert_allclose(e_out, ref, rtol=0, atol=1e-13)
+    assert np.any(np.abs(scale * q[dst] * k[src]) > 5.0)             # the clamp is exercised
+    with pytest.raises(orc.OracleError):
+        orc.forward(rp, ci, q, k, v, e, mode="standard", scale=scale, edge_ids=pe, want_e_out=True)
+
+
+@pytest.mark.parametrize("mode", ["standard", "clipped"])
+def test_edge_ids_indirection(orc, mode):
+    n, h, d = 70, 2, 16
+    src, dst = W.random_graph(911, 2, n, 10)
+    q, k, v, e = feats(22, n, src.shape[0], h, d, True)
+    rp, ci, pe = orc.build_csr(n, src, dst)
+    by_position = orc.forward(rp, ci, q, k, v, e[pe], mode=mode, scale=0.25)
+    by_edge_id = orc.forward(rp, ci, q, k, v, e, mode=mode, scale=0.25, edge_ids=pe)
+    assert np.array_equal(by_position, by_edge_id)
+
+
+@pytest.mark.parametrize("normalize", [False, True])
+@pytest.mark.parametrize("multi", [False, True])
+def test_aggregate_matches_scipy(orc, normalize, multi):
+    n, h, d = 90, 3, 8
+    src, dst = W.random_graph(912, 3, n, 14, multi=multi)
+    g = np.random.default_rng(5)
+    x = g.standard_normal((n, h, d))
+    w = g.random((src.shape[0], h)) + 0.1
+    rp, ci, pe = orc.build_csr(n, src, dst)
+    out = orc.aggregate(rp, ci, x, w, normalize=normalize, eps=1e-6, edge_ids=pe)
+    for hh in range(h):
+        A = sp.csr_matrix((w[:, hh], (dst, src)), shape=(n, n))          # repeated pairs add up
+        ref = A @ x[:, hh, :]
+        if normalize:
+            z = np.asarray(A.sum(axis=1)).ravel()
+            deg = np.bincount(dst, minlength=n)
+            ref = np.where(deg[:, None] > 0, ref / (z[:, None] + 1e-6), 0.0)
+        np.testing.assert_allclose(out[:, hh, :], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_aggregate_closed_form(orc):
+    wl = W.make(1)
+    x = wl.v().astype(np.float64)
+    rp, ci, pe = orc.build_csr(wl.num_nodes, wl.src, wl.dst)
+    ones = np.ones((wl.nnz, wl.heads))
+    mean, deg = neighbour_mean(wl.num_nodes, wl.src, wl.dst, x)
+    out = orc.aggregate(rp, ci, x, ones, normalize=True, eps=1e-6)
+    np.testing.assert_allclose(out, (deg / (deg + 1e-6))[:, None, None] * mean, rtol=1e-13, atol=1e-15)
+    out = orc.aggregate(rp, ci, x, ones, normalize=False)
+    np.testing.assert_allclose(out, deg[:, None, None] * mean, rtol=1e-13, atol=1e-13)

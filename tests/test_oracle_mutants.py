@@ -40,8 +40,14 @@ MUTANTS = {
     "edge_projection_ignored": (
         "s += qi[c] * kj[c] * (ep ? ep[c] : 1.0);", "s += qi[c] * kj[c];"),
     "edge_projection_reversed_in_row": (
-        "const double* ep = e ? e + (p * h + hh) * d : NULL;",
-        "const double* ep = e ? e + ((int64_t)(row_ptr[i + 1] - 1 - t) * h + hh) * d : NULL;"),
+        "const int64_t row = edge_ids ? (int64_t)edge_ids[p] : p;",
+        "const int64_t row = edge_ids ? (int64_t)edge_ids[p] : (int64_t)(row_ptr[i + 1] - 1 - t);"),
+    "edge_update_before_clamp": (
+        "        if (e_out) e_out[(row * h + hh) * d + c] = x;   /* the edge update before the sum */\n",
+        "        if (e_out) e_out[(row * h + hh) * d + c] = scale * qi[c] * kj[c] * (ep ? ep[c] : 1.0);\n"),
+    "aggregate_weight_of_position": (
+        "        const double wp = w[wrow * h + hh];", "        const double wp = w[(int64_t)p * h + hh];"),
+    "aggregate_normalised_without_eps": ("o[c] /= (z + eps);", "o[c] /= z;"),
     "csr_rows_descending": (
         "return (x > y) - (x < y);\n}\nstatic int cmp_i32",
         "return (x < y) - (x > y);\n}\nstatic int cmp_i32"),
@@ -66,6 +72,12 @@ def battery(orc):
     tfwd.test_sdpa_complete_digraphs(orc)
     tfwd.test_equal_logits_give_scipy_mean(orc, 1)
     tfwd.test_clipped_closed_forms(orc)
+    tfwd.test_e_out_is_the_elementwise_update(orc)
+    for mode in ("standard", "clipped"):
+        tfwd.test_edge_ids_indirection(orc, mode)
+    for normalize in (False, True):
+        tfwd.test_aggregate_matches_scipy(orc, normalize, True)
+    tfwd.test_aggregate_closed_form(orc)
     for mode in ("standard", "clipped"):
         tfwd.test_weights_sum(orc, mode)
         tfwd.test_invariants(orc, mode)
