@@ -6,8 +6,9 @@ current stream.  Names follow the C ABI in ``include/gattn.h``:
 
     gattn_build_csr(src, dst, num_nodes)            -> (row_ptr, col_idx, edge_perm)
     gattn_build_rowwindows(row_ptr, col_idx, n)     -> RowWindows
-    gattn_forward(row_ptr, col_idx, q, k, v, ...)   -> out [N, H, D]
+    gattn_forward(row_ptr, col_idx, q, k, v, ...)   -> out [N, H, D]  (, e_out)
     gattn_forward_path(...)                         -> "gather" | "mfma"
+    gattn_aggregate(row_ptr, col_idx, x, w, ...)    -> out [N, H, D]
 
 Importing this module raises if ``libgattn.so`` is missing: there is no
 fallback implementation.  Build it with ``python -m
@@ -58,6 +59,15 @@ class _ForwardArgs(ctypes.Structure):
                 ("out", ctypes.c_void_p), ("dtype", ctypes.c_int), ("mode", ctypes.c_int),
                 ("scale", ctypes.c_float), ("clip_lo", ctypes.c_float), ("clip_hi", ctypes.c_float),
                 ("eps", ctypes.c_float), ("path", ctypes.c_int), ("rw", ctypes.POINTER(_RowWindows)),
+                ("flags", ctypes.c_uint32), ("edge_ids", ctypes.c_void_p), ("e_out", ctypes.c_void_p)]
+
+
+class _AggregateArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("num_nodes", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("nnz", ctypes.c_int64),
+                ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p), ("x", ctypes.c_void_p),
+                ("w", ctypes.c_void_p), ("edge_ids", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("dtype", ctypes.c_int), ("normalize", ctypes.c_int32), ("eps", ctypes.c_float),
                 ("flags", ctypes.c_uint32)]
 
 
@@ -77,8 +87,9 @@ def _load():
                                          ctypes.c_size_t, vp]
     L.gattn_forward.argtypes = [ctypes.POINTER(_ForwardArgs), vp]
     L.gattn_forward_path.argtypes = [ctypes.POINTER(_ForwardArgs), ctypes.POINTER(ctypes.c_int)]
+    L.gattn_aggregate.argtypes = [ctypes.POINTER(_AggregateArgs), vp]
     for f in (L.gattn_build_csr_workspace, L.gattn_build_csr, L.gattn_build_rowwindows_workspace,
-              L.gattn_build_rowwindows, L.gattn_forward, L.gattn_forward_path):
+              L.gattn_build_rowwindows, L.gattn_forward, L.gattn_forward_path, L.gattn_aggregate):
         f.restype = st
     return L
 
@@ -202,7 +213,8 @@ def gattn_build_rowwindows(row_ptr: torch.Tensor, col_idx: torch.Tensor, num_nod
     return RowWindows(num_nodes, wcp, cols[:C], mask[:C].view(C // 16, 16) if C else mask[:0].view(0, 16))
 
 
-def _forward_args(row_ptr, col_idx, q, k, v, e, out, mode, scale, clip, eps, path, rw, validate):
+def _forward_args(row_ptr, col_idx, q, k, v, e, out, mode, scale, clip, eps, path, rw, validate,
+                  edge_ids=None, e_out=None):
     N, H, D = q.shape
     a = _ForwardArgs()
     a.struct_size = ctypes.sizeof(_ForwardArgs)
@@ -223,6 +235,8 @@ def _forward_args(row_ptr, col_idx, q, k, v, e, out, mode, scale, clip, eps, pat
         keep = rw._struct()
         a.rw = ctypes.pointer(keep)
     a.flags = GATTN_FLAG_VALIDATE if validate else 0
+    a.edge_ids = None if edge_ids is None else edge_ids.data_ptr()
+    a.e_out = None if e_out is None else e_out.data_ptr()
     return a, keep
 
 
@@ -234,9 +248,12 @@ def _check_node_tensor(t, name, like):
 def gattn_forward(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                   e: Optional[torch.Tensor] = None, mode: str = "standard", scale: Optional[float] = None,
                   clip=(-5.0, 5.0), eps: float = 1e-6, path: str = "auto", rw: Optional[RowWindows] = None,
-                  out: Optional[torch.Tensor] = None, validate: bool = False) -> torch.Tensor:
+                  out: Optional[torch.Tensor] = None, validate: bool = False,
+                  edge_ids: Optional[torch.Tensor] = None, e_out=None):
     """Fused SDDMM -> softmax -> SpMM over the CSR; q/k/v [N, H, D]; e
-    [nnz, H, D] by CSR position or None.  Returns out [N, H, D]."""
+    [nnz, H, D] by CSR position (or row edge_ids[p] for position p) or None.
+    Returns out [N, H, D]; with e_out (True, or an [nnz, H, D] tensor) the
+    clipped mode also writes the per-edge update and returns (out, e_out)."""
     row_ptr, col_idx = _i32(row_ptr, "row_ptr"), _i32(col_idx, "col_idx")
     if q.dim() != 3 or not q.is_contiguous() or not q.is_cuda:
         raise ValueError("q must be a contiguous [N, H, D] GPU tensor")
@@ -245,14 +262,25 @@ def gattn_forward(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch.Tensor,
     N, H, D = q.shape
     if e is not None and (e.dtype != q.dtype or tuple(e.shape) != (col_idx.numel(), H, D) or not e.is_contiguous()):
         raise ValueError("e must be a contiguous [nnz, H, D] tensor of q's dtype")
+    if edge_ids is not None:
+        edge_ids = _i32(edge_ids, "edge_ids")
+        if edge_ids.numel() != col_idx.numel():
+            raise ValueError("edge_ids must have one entry per edge")
+    want_e_out = e_out is not None and e_out is not False
+    if e_out is True:
+        e_out = torch.empty((col_idx.numel(), H, D), dtype=q.dtype, device=q.device)
+    elif want_e_out and (e_out.dtype != q.dtype or tuple(e_out.shape) != (col_idx.numel(), H, D)
+                         or not e_out.is_contiguous()):
+        raise ValueError("e_out must be a contiguous [nnz, H, D] tensor of q's dtype")
     if out is None:
         out = torch.empty_like(q)
     else:
         _check_node_tensor(out, "out", q)
-    a, keep = _forward_args(row_ptr, col_idx, q, k, v, e, out, mode, scale, clip, eps, path, rw, validate)
+    a, keep = _forward_args(row_ptr, col_idx, q, k, v, e, out, mode, scale, clip, eps, path, rw, validate,
+                            edge_ids, e_out if want_e_out else None)
     _check(_lib.gattn_forward(ctypes.byref(a), _stream(q.device)), "gattn_forward")
     del keep
-    return out
+    return (out, e_out) if want_e_out else out
 
 
 def gattn_forward_path(row_ptr, col_idx, q, k, v, e=None, mode="standard", path="auto",
@@ -264,5 +292,40 @@ def gattn_forward_path(row_ptr, col_idx, q, k, v, e=None, mode="standard", path=
     return _PATH_NAMES[res.value]
 
 
-__all__ = ["gattn_build_csr", "gattn_build_rowwindows", "gattn_forward", "gattn_forward_path",
+def gattn_aggregate(row_ptr: torch.Tensor, col_idx: torch.Tensor, x: torch.Tensor, w: torch.Tensor,
+                    normalize: bool = False, eps: float = 1e-6, edge_ids: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, validate: bool = False) -> torch.Tensor:
+    """Weighted aggregation over the CSR: x [N, H, D], w [nnz, H] fp32 (row
+    edge_ids[p] for position p when given); out[i] = sum_p w x[src], divided
+    by (sum_p w + eps) when normalize."""
+    row_ptr, col_idx = _i32(row_ptr, "row_ptr"), _i32(col_idx, "col_idx")
+    if x.dim() != 3 or not x.is_contiguous() or not x.is_cuda or x.dtype not in _DTYPES:
+        raise ValueError("x must be a contiguous [N, H, D] GPU tensor")
+    N, H, D = x.shape
+    nnz = col_idx.numel()
+    if w.dtype != torch.float32 or tuple(w.shape) != (nnz, H) or not w.is_contiguous() or w.device != x.device:
+        raise ValueError("w must be a contiguous fp32 [nnz, H] tensor on x's device")
+    if edge_ids is not None:
+        edge_ids = _i32(edge_ids, "edge_ids")
+        if edge_ids.numel() != nnz:
+            raise ValueError("edge_ids must have one entry per edge")
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _check_node_tensor(out, "out", x)
+    a = _AggregateArgs()
+    a.struct_size = ctypes.sizeof(_AggregateArgs)
+    a.num_nodes, a.num_heads, a.head_dim, a.nnz = N, H, D, nnz
+    a.row_ptr, a.col_idx = row_ptr.data_ptr(), col_idx.data_ptr()
+    a.x, a.w, a.out = x.data_ptr(), w.data_ptr(), out.data_ptr()
+    a.edge_ids = None if edge_ids is None else edge_ids.data_ptr()
+    a.dtype = _DTYPES[x.dtype]
+    a.normalize = 1 if normalize else 0
+    a.eps = eps
+    a.flags = GATTN_FLAG_VALIDATE if validate else 0
+    _check(_lib.gattn_aggregate(ctypes.byref(a), _stream(x.device)), "gattn_aggregate")
+    return out
+
+
+__all__ = ["gattn_build_csr", "gattn_build_rowwindows", "gattn_forward", "gattn_forward_path", "gattn_aggregate",
            "gattn_status_string", "gattn_abi_version", "CsrBuilder", "RowWindows", "GattnError", "LIB_PATH"]

@@ -13,7 +13,8 @@
 using namespace gattn;
 
 // the Python binding mirrors these layouts with ctypes
-static_assert(sizeof(gattn_forward_args) == 128, "gattn_forward_args layout");
+static_assert(sizeof(gattn_forward_args) == 144, "gattn_forward_args layout");
+static_assert(sizeof(gattn_aggregate_args) == 88, "gattn_aggregate_args layout");
 static_assert(sizeof(gattn_rowwindows) == 40, "gattn_rowwindows layout");
 
 namespace {
@@ -44,19 +45,54 @@ gattn_status check_forward(const gattn_forward_args* a, bool launch) {
   if (a->mode == GATTN_SOFTMAX_CLIPPED) {
     if (!(a->clip_lo <= a->clip_hi) || !(a->eps >= 0.f) || !(a->eps < INFINITY)) return GATTN_ERR_INVALID_VALUE;
   }
+  // the edge update exists in the clipped mode with an edge projection only
+  if (a->e_out && (a->mode != GATTN_SOFTMAX_CLIPPED || !a->e)) return GATTN_ERR_INVALID_VALUE;
   if (a->head_dim != 16 && a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128) return GATTN_ERR_UNSUPPORTED;
   if ((int64_t)a->num_heads * a->head_dim > (int64_t)1 << 20) return GATTN_ERR_UNSUPPORTED;
   if (a->num_nodes == 0) return GATTN_OK;
   if (!a->row_ptr || !a->q || !a->k || !a->v || (launch && !a->out)) return GATTN_ERR_INVALID_VALUE;
   if (a->nnz > 0 && !a->col_idx) return GATTN_ERR_INVALID_VALUE;
-  if (!aligned(a->row_ptr, 4) || !aligned(a->col_idx, 4)) return GATTN_ERR_INVALID_VALUE;
-  const void* t[] = {a->q, a->k, a->v, a->e, a->out};
+  if (!aligned(a->row_ptr, 4) || !aligned(a->col_idx, 4) || !aligned(a->edge_ids, 4)) return GATTN_ERR_INVALID_VALUE;
+  const void* t[] = {a->q, a->k, a->v, a->e, a->out, a->e_out};
   for (const void* p : t)
     if (!aligned(p, 16)) return GATTN_ERR_INVALID_VALUE;
   const size_t node_bytes = (size_t)a->num_nodes * a->num_heads * a->head_dim * elem_size(a->dtype);
   const size_t edge_bytes = (size_t)a->nnz * a->num_heads * a->head_dim * elem_size(a->dtype);
   if (overlap(a->out, node_bytes, a->q, node_bytes) || overlap(a->out, node_bytes, a->k, node_bytes) ||
       overlap(a->out, node_bytes, a->v, node_bytes) || overlap(a->out, node_bytes, a->e, edge_bytes))
+    return GATTN_ERR_INVALID_VALUE;
+  if (a->e_out && a->nnz > 0) {
+    const size_t ib = (size_t)a->nnz * 4;
+    if (overlap(a->e_out, edge_bytes, a->q, node_bytes) || overlap(a->e_out, edge_bytes, a->k, node_bytes) ||
+        overlap(a->e_out, edge_bytes, a->v, node_bytes) || overlap(a->e_out, edge_bytes, a->e, edge_bytes) ||
+        overlap(a->e_out, edge_bytes, a->out, node_bytes) || overlap(a->e_out, edge_bytes, a->row_ptr, 4 * ((size_t)a->num_nodes + 1)) ||
+        overlap(a->e_out, edge_bytes, a->col_idx, ib) || overlap(a->e_out, edge_bytes, a->edge_ids, ib))
+      return GATTN_ERR_INVALID_VALUE;
+  }
+  return GATTN_OK;
+}
+
+gattn_status check_aggregate(const gattn_aggregate_args* a) {
+  if (!a || a->struct_size != sizeof(gattn_aggregate_args)) return GATTN_ERR_INVALID_VALUE;
+  if (a->num_nodes < 0 || a->num_heads < 1 || a->nnz < 0 || a->nnz > INT32_MAX) return GATTN_ERR_INVALID_VALUE;
+  if (a->dtype != GATTN_F32 && a->dtype != GATTN_F16 && a->dtype != GATTN_BF16) return GATTN_ERR_INVALID_VALUE;
+  if (a->normalize != 0 && a->normalize != 1) return GATTN_ERR_INVALID_VALUE;
+  if (!(a->eps >= 0.f) || !(a->eps < INFINITY)) return GATTN_ERR_INVALID_VALUE;
+  if (a->flags & ~GATTN_FLAG_VALIDATE) return GATTN_ERR_INVALID_VALUE;
+  if (a->head_dim != 16 && a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128) return GATTN_ERR_UNSUPPORTED;
+  if ((int64_t)a->num_heads * a->head_dim > (int64_t)1 << 20) return GATTN_ERR_UNSUPPORTED;
+  if (a->num_nodes == 0) return GATTN_OK;
+  if (!a->row_ptr || !a->x || !a->out) return GATTN_ERR_INVALID_VALUE;
+  if (a->nnz > 0 && (!a->col_idx || !a->w)) return GATTN_ERR_INVALID_VALUE;
+  if (!aligned(a->row_ptr, 4) || !aligned(a->col_idx, 4) || !aligned(a->edge_ids, 4) || !aligned(a->w, 4))
+    return GATTN_ERR_INVALID_VALUE;
+  if (!aligned(a->x, 16) || !aligned(a->out, 16)) return GATTN_ERR_INVALID_VALUE;
+  const size_t node_bytes = (size_t)a->num_nodes * a->num_heads * a->head_dim * elem_size(a->dtype);
+  if (overlap(a->out, node_bytes, a->x, node_bytes) ||
+      overlap(a->out, node_bytes, a->w, (size_t)a->nnz * a->num_heads * 4) ||
+      overlap(a->out, node_bytes, a->row_ptr, 4 * ((size_t)a->num_nodes + 1)) ||
+      overlap(a->out, node_bytes, a->col_idx, (size_t)a->nnz * 4) ||
+      overlap(a->out, node_bytes, a->edge_ids, (size_t)a->nnz * 4))
     return GATTN_ERR_INVALID_VALUE;
   return GATTN_OK;
 }
@@ -89,18 +125,30 @@ gattn_status resolve(const gattn_forward_args* a, gattn_path* out) {
   return GATTN_OK;
 }
 
-// GATTN_FLAG_VALIDATE: copy the index arrays to the host and check them
-gattn_status validate_graph(const gattn_forward_args* a, hipStream_t s) {
-  std::vector<int32_t> rp((size_t)a->num_nodes + 1), ci((size_t)a->nnz);
-  if (hipMemcpyAsync(rp.data(), a->row_ptr, rp.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess) return GATTN_ERR_HIP;
-  if (a->nnz && hipMemcpyAsync(ci.data(), a->col_idx, ci.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess)
+// GATTN_FLAG_VALIDATE: copy the index arrays to the host and check them.
+// ids (nullable) must lie in [0, nnz); with `permutation` each id once.
+gattn_status validate_graph(int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                            const int32_t* ids, bool permutation, hipStream_t s) {
+  std::vector<int32_t> rp((size_t)n + 1), ci((size_t)nnz), id(ids ? (size_t)nnz : 0);
+  if (hipMemcpyAsync(rp.data(), row_ptr, rp.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess) return GATTN_ERR_HIP;
+  if (nnz && hipMemcpyAsync(ci.data(), col_idx, ci.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return GATTN_ERR_HIP;
+  if (nnz && ids && hipMemcpyAsync(id.data(), ids, id.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess)
     return GATTN_ERR_HIP;
   if (hipStreamSynchronize(s) != hipSuccess) return GATTN_ERR_HIP;
-  if (rp[0] != 0 || rp[a->num_nodes] != a->nnz) return GATTN_ERR_BAD_GRAPH;
-  for (int32_t i = 0; i < a->num_nodes; ++i)
+  if (rp[0] != 0 || rp[n] != nnz) return GATTN_ERR_BAD_GRAPH;
+  for (int32_t i = 0; i < n; ++i)
     if (rp[i + 1] < rp[i]) return GATTN_ERR_BAD_GRAPH;
   for (int32_t c : ci)
-    if (c < 0 || c >= a->num_nodes) return GATTN_ERR_BAD_GRAPH;
+    if (c < 0 || c >= n) return GATTN_ERR_BAD_GRAPH;
+  std::vector<uint8_t> seen(permutation ? id.size() : 0, 0);
+  for (int32_t r : id) {
+    if (r < 0 || r >= nnz) return GATTN_ERR_BAD_GRAPH;
+    if (permutation) {
+      if (seen[r]) return GATTN_ERR_BAD_GRAPH;
+      seen[r] = 1;
+    }
+  }
   return GATTN_OK;
 }
 
@@ -214,10 +262,29 @@ gattn_status gattn_forward(const gattn_forward_args* args, hipStream_t stream) {
     if ((st = resolve(args, &path)) != GATTN_OK) return st;
     if (args->num_nodes == 0) return GATTN_OK;
     if (args->flags & GATTN_FLAG_VALIDATE) {
-      if ((st = validate_graph(args, stream)) != GATTN_OK) return st;
+      const int32_t* ids = args->e ? args->edge_ids : nullptr;  // read only with an edge tensor
+      if ((st = validate_graph(args->num_nodes, args->nnz, args->row_ptr, args->col_idx, ids, args->e_out != nullptr,
+                               stream)) != GATTN_OK)
+        return st;
     }
     if (path == GATTN_PATH_MFMA) return from_hip(launch_forward_mfma(*args, stream));
     return from_hip(launch_forward_gather(*args, stream));
+  } catch (...) {
+    return GATTN_ERR_HIP;
+  }
+}
+
+gattn_status gattn_aggregate(const gattn_aggregate_args* args, hipStream_t stream) {
+  try {
+    gattn_status st = check_aggregate(args);
+    if (st != GATTN_OK) return st;
+    if (args->num_nodes == 0) return GATTN_OK;
+    if (args->flags & GATTN_FLAG_VALIDATE) {
+      if ((st = validate_graph(args->num_nodes, args->nnz, args->row_ptr, args->col_idx, args->edge_ids, false,
+                               stream)) != GATTN_OK)
+        return st;
+    }
+    return from_hip(launch_aggregate_gather(*args, stream));
   } catch (...) {
     return GATTN_ERR_HIP;
   }

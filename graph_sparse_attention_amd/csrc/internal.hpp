@@ -41,6 +41,7 @@ hipError_t launch_rowwindows_fill(int32_t n, int64_t nnz, const int32_t* row_ptr
 // Forward -------------------------------------------------------------------
 hipError_t launch_forward_gather(const gattn_forward_args& a, hipStream_t s);
 hipError_t launch_forward_mfma(const gattn_forward_args& a, hipStream_t s);
+hipError_t launch_aggregate_gather(const gattn_aggregate_args& a, hipStream_t s);
 // applicability of the MFMA row-window path (no launch)
 bool mfma_supported(const gattn_forward_args& a);
 

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GATTN_ABI_VERSION 1
+#define GATTN_ABI_VERSION 2
 
 #ifndef GATTN_API
 #define GATTN_API __attribute__((visibility("default")))
@@ -166,7 +166,7 @@ typedef struct {
   const void* q;               /* [N, H, D] contiguous, `dtype`, 16-byte aligned     */
   const void* k;               /* [N, H, D]                                          */
   const void* v;               /* [N, H, D]                                          */
-  const void* e;               /* nullable; [nnz, H, D] by CSR position              */
+  const void* e;               /* nullable; [nnz, H, D] by CSR position (or edge_ids) */
   void* out;                   /* [N, H, D] `dtype`; must not alias the inputs       */
   gattn_dtype dtype;           /* of q, k, v, e and out; arithmetic is fp32          */
   gattn_mode mode;
@@ -176,6 +176,20 @@ typedef struct {
   gattn_path path;             /* AUTO picks MFMA when it applies and rw is given    */
   const gattn_rowwindows* rw;  /* [host] struct of device arrays; MFMA path only     */
   uint32_t flags;              /* GATTN_FLAG_*                                       */
+  /* Edge-id indirection (the article's map from CSC position to edge id):
+     nullable [nnz] int32; when set, the per-edge rows of e and e_out are
+     e[edge_ids[p]] for CSR position p (pass gattn_build_csr's edge_perm to keep
+     E in the caller's original edge order).  Values must lie in [0, nnz), and
+     form a permutation when e_out is given (two positions writing one row
+     race).  GATTN_FLAG_VALIDATE checks both on the host (GATTN_ERR_BAD_GRAPH);
+     unchecked, an out-of-range id is clamped into range (no fault, the
+     result is unspecified).  Read only when e is given.                       */
+  const int32_t* edge_ids;
+  /* RTMScore edge update (the article's e_out): nullable [nnz, H, D] `dtype`,
+     clipped mode with e only; row r = edge_ids ? edge_ids[p] : p receives
+     clamp(scale * q[dst] * k[src], clip_lo, clip_hi) * e[r], the product before
+     the feature sum.  Must not alias any input or out.                         */
+  void* e_out;
 } gattn_forward_args;
 
 /* out[i, h, :] = sum_p alpha_p(h) v[col_idx[p], h, :] over the in-edges p of i;
@@ -187,6 +201,38 @@ GATTN_API gattn_status gattn_forward(const gattn_forward_args* args /*[host]*/, 
 
 /* The path gattn_forward would take for these arguments (no work enqueued; `out` may be NULL). */
 GATTN_API gattn_status gattn_forward_path(const gattn_forward_args* args /*[host]*/, gattn_path* path /*[host]*/);
+
+/* ------------------------------------------------------------------------
+ * gattn_aggregate: weighted aggregation over the CSR with given per-edge
+ * weights (no logits, no softmax) -- the POPCORNBENCH CSR problem
+ *   out[i, h, :] = sum_p w[r(p), h] * x[col_idx[p], h, :],  r(p) = edge_ids ? edge_ids[p] : p,
+ * and, with normalize = 1, the gattn-triton article's scatter add of scaled
+ * values and scores followed by numerator / (denominator + eps)
+ *   out[i, h, :] = (sum_p w x) / (sum_p w + eps).
+ * A destination without in-edges gets exactly 0.  Same kernels, balance and
+ * determinism as the gather path of gattn_forward.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  uint32_t struct_size;        /* sizeof(gattn_aggregate_args)                       */
+  int32_t num_nodes;           /* N >= 0                                             */
+  int32_t num_heads;           /* H >= 1                                             */
+  int32_t head_dim;            /* D in {16, 32, 64, 128}                             */
+  int64_t nnz;
+  const int32_t* row_ptr;      /* [N+1] CSR by destination                           */
+  const int32_t* col_idx;      /* [nnz]                                              */
+  const void* x;               /* [N, H, D] `dtype`, 16-byte aligned                 */
+  const float* w;              /* [nnz, H] fp32 weights                              */
+  const int32_t* edge_ids;     /* nullable [nnz]: row of w for CSR position p, in
+                                  [0, nnz) (checked with GATTN_FLAG_VALIDATE, else
+                                  clamped)                                          */
+  void* out;                   /* [N, H, D] `dtype`; must not alias the inputs       */
+  gattn_dtype dtype;
+  int32_t normalize;           /* 0: weighted sum; 1: divided by (sum of w + eps)    */
+  float eps;                   /* >= 0                                               */
+  uint32_t flags;              /* GATTN_FLAG_VALIDATE                                */
+} gattn_aggregate_args;
+
+GATTN_API gattn_status gattn_aggregate(const gattn_aggregate_args* args /*[host]*/, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(gsa):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     lib = ctypes.CDLL(gsa.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), f"{name} declared in gattn.h but not exported"
@@ -46,10 +46,11 @@ def test_enums_and_strings(gsa):
                  "GATTN_ERR_DUPLICATE_EDGE", "GATTN_ERR_BUFFER_TOO_SMALL", "GATTN_ERR_HIP"]:
         m = re.search(name + r"\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(gsa, name)
-    assert gsa.gattn_abi_version() == 1
+    assert gsa.gattn_abi_version() == 2
     assert gsa.gattn_status_string(gsa.GATTN_ERR_DUPLICATE_EDGE).startswith("repeated")
     assert gsa.gattn_status_string(99) == "unknown status"
-    assert ctypes.sizeof(gsa._ForwardArgs) == 128
+    assert ctypes.sizeof(gsa._ForwardArgs) == 144
+    assert ctypes.sizeof(gsa._AggregateArgs) == 88
 
 
 def fake_args(gsa, **kw):
@@ -96,6 +97,15 @@ def test_forward_argument_errors(gsa):
         (dict(path=gsa.GATTN_PATH_MFMA, dtype=gsa.GATTN_F32), gsa.GATTN_ERR_UNSUPPORTED),
         (dict(path=gsa.GATTN_PATH_MFMA, mode=gsa.GATTN_SOFTMAX_CLIPPED), gsa.GATTN_ERR_UNSUPPORTED),
         (dict(path=gsa.GATTN_PATH_MFMA, head_dim=16), gsa.GATTN_ERR_UNSUPPORTED),
+        # the edge update needs the clipped mode and an edge tensor, no aliasing
+        (dict(e_out=(1 << 32) + (16 << 20)), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(e_out=(1 << 32) + (16 << 20), mode=gsa.GATTN_SOFTMAX_CLIPPED), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(e_out=(1 << 32) + (16 << 20), e=(1 << 32) + (14 << 20)), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(e_out=(1 << 32) + (14 << 20) + 64, e=(1 << 32) + (14 << 20), mode=gsa.GATTN_SOFTMAX_CLIPPED),
+         gsa.GATTN_ERR_INVALID_VALUE),                                 # aliases e
+        (dict(e_out=(1 << 32) + (16 << 20) + 8, e=(1 << 32) + (14 << 20), mode=gsa.GATTN_SOFTMAX_CLIPPED),
+         gsa.GATTN_ERR_INVALID_VALUE),                                 # misaligned
+        (dict(edge_ids=(1 << 32) + 2), gsa.GATTN_ERR_INVALID_VALUE),   # misaligned
     ]
     for kw, want in cases:
         a = fake_args(gsa, **kw)
@@ -143,3 +153,47 @@ def test_build_argument_errors(gsa):
     assert L.gattn_build_rowwindows(10, 20, p(1), p(2), p(3), None, None, None, p(6), need, None) == 1
     assert L.gattn_build_rowwindows(10, 20, None, p(2), p(3), None, None, ctypes.byref(nc), p(6), need, None) == 1
     assert L.gattn_build_rowwindows(10, 20, p(1), p(2), p(3), None, None, ctypes.byref(nc), p(6), need - 8, None) == 5
+
+
+def fake_aggregate(gsa, **kw):
+    a = gsa._AggregateArgs()
+    a.struct_size = ctypes.sizeof(gsa._AggregateArgs)
+    a.num_nodes, a.num_heads, a.head_dim, a.nnz = 100, 8, 64, 1000
+    base = 1 << 32
+    a.row_ptr, a.col_idx, a.x, a.w = base, base + (1 << 20), base + (2 << 20), base + (4 << 20)
+    a.edge_ids, a.out = None, base + (6 << 20)
+    a.dtype, a.normalize, a.eps, a.flags = gsa.GATTN_F32, 0, 1e-6, 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_aggregate_argument_errors(gsa):
+    L = gsa._lib
+    base = 1 << 32
+    cases = [
+        (dict(struct_size=8), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(num_nodes=-2), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(num_heads=0), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(nnz=1 << 31), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(dtype=3), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(normalize=2), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(eps=-1e-3), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(eps=float("inf")), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(flags=4), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(head_dim=8), gsa.GATTN_ERR_UNSUPPORTED),
+        (dict(w=None), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(x=None), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(out=None), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(x=base + (2 << 20) + 4), gsa.GATTN_ERR_INVALID_VALUE),     # misaligned
+        (dict(w=base + (4 << 20) + 2), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(out=base + (2 << 20) + 4096), gsa.GATTN_ERR_INVALID_VALUE),  # aliases x
+        (dict(out=base + (4 << 20)), gsa.GATTN_ERR_INVALID_VALUE),         # aliases w
+    ]
+    for kw, want in cases:
+        a = fake_aggregate(gsa, **kw)
+        assert L.gattn_aggregate(ctypes.byref(a), None) == want, kw
+    assert L.gattn_aggregate(None, None) == gsa.GATTN_ERR_INVALID_VALUE
+    # nothing to do: no launch, no HIP call
+    a = fake_aggregate(gsa, num_nodes=0, nnz=0, row_ptr=None, x=None, w=None, out=None)
+    assert L.gattn_aggregate(ctypes.byref(a), None) == gsa.GATTN_OK
