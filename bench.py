@@ -17,6 +17,12 @@ and the HIP events around each kernel measure the kernel, not host gaps.
 Output: one JSON line (metric, value in GEdges/s of the whole step, roofline
 of the forward kernel against 8 TB/s HBM, the CPU oracle's rate on the host).
 
+--variant picks what follows the CSR build (default: forward):
+    e_out      the forward also writes the RTMScore per-edge update
+    edge_ids   E stays in COO order and is read through the CSR's edge_perm
+    aggregate  gattn_aggregate: V summed with seeded fp32 weights per edge and
+               head, normalized by the summed weights + eps (no logits)
+
 Counter mode (used under rocprofv3 --pmc):
     python bench.py --counters-run        one copy kernel of known size, then
                                           forward launches, no timing
@@ -49,6 +55,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = {"gather": "graph_sparse_attention_amd/csrc/forward_gather.hip",
               "mfma": "graph_sparse_attention_amd/csrc/forward_mfma.hip"}
 COPY_BYTES = 512 << 20      # calibration copy for the traffic counters
+VARIANTS = {"forward": "gattn_forward", "e_out": "gattn_forward + edge update",
+            "edge_ids": "gattn_forward, E through edge ids", "aggregate": "gattn_aggregate (normalized)"}
 
 
 def parse():
@@ -58,6 +66,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", type=int, default=2)
     p.add_argument("--path", default="auto", choices=["auto", "gather", "mfma"])
+    p.add_argument("--variant", default="forward", choices=list(VARIANTS))
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bound of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--counters-run", action="store_true")
@@ -74,10 +83,20 @@ def src_hash(path_key):
 # workload and algorithmic bytes
 # ---------------------------------------------------------------------------
 
-def algorithmic_bytes(n, nnz, h, d, s, has_e):
-    """Compulsory HBM bytes of one forward: every input once, output once.
-    B_min = 4(N+1) + 4 nnz + 3 N H D s + nnz H D s [E] + N H D s."""
-    return 4 * (n + 1) + 4 * nnz + 3 * n * h * d * s + (nnz * h * d * s if has_e else 0) + n * h * d * s
+def algorithmic_bytes(n, nnz, h, d, s, has_e, variant="forward"):
+    """Compulsory HBM bytes of one launch: every input once, output once.
+    forward:   B_min = 4(N+1) + 4 nnz + 3 N H D s + nnz H D s [E] + N H D s
+    e_out:     B_min + nnz H D s (the edge update written)
+    edge_ids:  B_min + 4 nnz (the id per edge)
+    aggregate: 4(N+1) + 4 nnz + N H D s (x) + 4 nnz H (w) + N H D s (out)"""
+    if variant == "aggregate":
+        return 4 * (n + 1) + 4 * nnz + n * h * d * s + 4 * nnz * h + n * h * d * s
+    b = 4 * (n + 1) + 4 * nnz + 3 * n * h * d * s + (nnz * h * d * s if has_e else 0) + n * h * d * s
+    if variant == "e_out":
+        b += nnz * h * d * s
+    elif variant == "edge_ids":
+        b += 4 * nnz
+    return b
 
 
 class Batch:
@@ -89,39 +108,51 @@ class Batch:
         self.q, self.k, self.v = (host[x].to(dev) for x in ("q", "k", "v"))
         self.e = host["e"].to(dev) if host["e"] is not None else None
         self.out = torch.empty_like(self.q)
+        self.w = host["w"].to(dev) if host.get("w") is not None else None
+        self.e_out = torch.empty_like(self.e) if host.get("e_out") and self.e is not None else None
         self.csr = gsa.CsrBuilder(wl.num_nodes, wl.nnz, dev)
         self.rw = None
 
 
-def make_host_inputs(wl):
+def make_host_inputs(wl, variant="forward"):
     import torch
     import workloads as W
     h = {"src": torch.from_numpy(wl.src), "dst": torch.from_numpy(wl.dst)}
     for x in ("q", "k", "v"):
         h[x] = W.cast(getattr(wl, x)(), wl.dtype)
     h["e"] = W.cast(wl.e(), wl.dtype) if wl.has_e else None
+    if variant == "aggregate":
+        h["w"] = torch.from_numpy(wl.w())
+    h["e_out"] = variant == "e_out"
     return h
 
 
-def batch_bytes(wl, es):
+def batch_bytes(wl, es, variant="forward"):
     n, m, hd = wl.num_nodes, wl.nnz, wl.heads * wl.head_dim
-    return 8 * m + 4 * n + 8 * m + 4 * n * hd * es + (m * hd * es if wl.has_e else 0)
+    e = m * hd * es if wl.has_e else 0
+    return 8 * m + 4 * n + 8 * m + 4 * n * hd * es + e * (2 if variant == "e_out" else 1) + \
+        (4 * m * wl.heads if variant == "aggregate" else 0)
 
 
 # ---------------------------------------------------------------------------
 # CPU oracle baseline
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(wl, host, seconds):
+def cpu_baseline(wl, host, seconds, variant="forward"):
     import oracle
     cores = len(os.sched_getaffinity(0))
     q64, k64, v64 = (oracle.widen(host[x]) for x in ("q", "k", "v"))
     e64 = oracle.widen(host["e"]) if host["e"] is not None else None
+    w64 = host["w"].numpy().astype(np.float64) if variant == "aggregate" else None
     reps, t0 = 0, time.perf_counter()
     while True:
         rp, ci, pe = oracle.build_csr(wl.num_nodes, wl.src, wl.dst)
-        oracle.forward(rp, ci, q64, k64, v64, e64, mode=wl.mode, scale=wl.scale, clip=wl.clip, eps=wl.eps,
-                       threads=cores)
+        if variant == "aggregate":
+            oracle.aggregate(rp, ci, v64, w64, normalize=True, eps=wl.eps, threads=cores)
+        else:
+            oracle.forward(rp, ci, q64, k64, v64, e64, mode=wl.mode, scale=wl.scale, clip=wl.clip, eps=wl.eps,
+                           threads=cores, edge_ids=pe if variant == "edge_ids" else None,
+                           want_e_out=variant == "e_out")
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 100000:
@@ -135,7 +166,7 @@ def cpu_baseline(wl, host, seconds):
     except OSError:
         pass
     return {"value": round(wl.nnz * reps / el / 1e9, 6), "unit": "GEdges/s", "cores": cores, "kind": "oracle",
-            "sample": f"the full batch ({wl.nnz} edges), oracle CSR build (1 thread) + fp64 forward "
+            "sample": f"the full batch ({wl.nnz} edges), oracle CSR build (1 thread) + fp64 {VARIANTS[variant]} "
                       f"({cores} OpenMP threads), repeated {reps}x in {el:.1f} s; host CPU: {cpu_model}"}
 
 
@@ -143,12 +174,14 @@ def cpu_baseline(wl, host, seconds):
 # counters
 # ---------------------------------------------------------------------------
 
-def counters_file(path_key, config):
-    return os.path.join(PROFILES, f"{'forward_gather' if path_key == 'gather' else 'forward_mfma'}_config{config}_counters.json")
+def counters_file(path_key, config, variant="forward"):
+    suffix = "" if variant == "forward" else f"_{variant}"
+    return os.path.join(PROFILES, f"{'forward_gather' if path_key == 'gather' else 'forward_mfma'}"
+                                  f"_config{config}{suffix}_counters.json")
 
 
-def load_traffic(path_key, config):
-    f = counters_file(path_key, config)
+def load_traffic(path_key, config, variant="forward"):
+    f = counters_file(path_key, config, variant)
     if not os.path.exists(f):
         return None
     d = json.load(open(f))
@@ -157,7 +190,7 @@ def load_traffic(path_key, config):
     return d
 
 
-def ingest_counters(dirname, config, path_key):
+def ingest_counters(dirname, config, path_key, variant="forward"):
     """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the forward kernel
     and of the calibration copy; scale by the copy's bytes-per-count."""
     rows = []
@@ -182,14 +215,14 @@ def ingest_counters(dirname, config, path_key):
     copy_write = res.get("copy_WRITE_SIZE")
     fr = COPY_BYTES / (copy_read * 1024.0) if copy_read else None
     fw = COPY_BYTES / (copy_write * 1024.0) if copy_write else None
-    out = {"kernel": kern, "config": config, "kernel_source_sha256_16": src_hash(path_key),
+    out = {"kernel": kern, "config": config, "variant": variant, "kernel_source_sha256_16": src_hash(path_key),
            "fetch_kib_per_dispatch": res.get("fwd_FETCH_SIZE"), "write_kib_per_dispatch": res.get("fwd_WRITE_SIZE"),
            "copy_fetch_kib": copy_read, "copy_write_kib": copy_write, "copy_bytes_each_way": COPY_BYTES,
            "read_scale": fr, "write_scale": fw}
     if res.get("fwd_FETCH_SIZE") is not None and fr and res.get("fwd_WRITE_SIZE") is not None and fw:
         out["hbm_bytes_per_launch"] = res["fwd_FETCH_SIZE"] * 1024.0 * fr + res["fwd_WRITE_SIZE"] * 1024.0 * fw
     os.makedirs(PROFILES, exist_ok=True)
-    with open(counters_file(path_key, config), "w") as fh:
+    with open(counters_file(path_key, config, variant), "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out))
 
@@ -205,7 +238,7 @@ def main():
     import workloads as W
     if args.ingest_counters:
         path_key = "mfma" if args.path == "mfma" else "gather"
-        ingest_counters(args.ingest_counters, args.config, path_key)
+        ingest_counters(args.ingest_counters, args.config, path_key, args.variant)
         return
 
     import torch
@@ -214,8 +247,20 @@ def main():
     torch.cuda.set_device(dev)
     print(f"# generating workload config {args.config}", file=sys.stderr, flush=True)
     wl = W.make(args.config)
-    host = make_host_inputs(wl)
+    if args.variant in ("e_out", "edge_ids") and not wl.has_e:
+        sys.exit(f"--variant {args.variant} needs a workload with an edge tensor (config 2)")
+    if args.variant == "e_out" and wl.mode != "clipped":
+        sys.exit("--variant e_out needs the clipped softmax (config 2)")
+    host = make_host_inputs(wl, args.variant)
     es = 4 if wl.dtype == "f32" else 2
+
+    def run_op(b, rp, ci, pe):
+        if args.variant == "aggregate":
+            gsa.gattn_aggregate(rp, ci, b.v, b.w, normalize=True, eps=wl.eps, out=b.out)
+        else:
+            gsa.gattn_forward(rp, ci, b.q, b.k, b.v, b.e, mode=wl.mode, scale=wl.scale, clip=wl.clip, eps=wl.eps,
+                              path=args.path, rw=b.rw, out=b.out,
+                              edge_ids=pe if args.variant == "edge_ids" else None, e_out=b.e_out)
 
     if args.counters_run:
         a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -225,34 +270,32 @@ def main():
         b.copy_(a)                      # calibration: COPY_BYTES read + COPY_BYTES written (runtime copyBuffer kernel)
         torch.cuda.synchronize()
         bt = Batch(wl, dev, host)
-        rp, ci, _ = bt.csr(bt.src, bt.dst)
-        rw = gsa.gattn_build_rowwindows(rp, ci, wl.num_nodes) if args.path == "mfma" else None
+        rp, ci, pe = bt.csr(bt.src, bt.dst)
+        bt.rw = gsa.gattn_build_rowwindows(rp, ci, wl.num_nodes) if args.path == "mfma" else None
         for _ in range(5):
-            gsa.gattn_forward(rp, ci, bt.q, bt.k, bt.v, bt.e, mode=wl.mode, scale=wl.scale, clip=wl.clip,
-                              eps=wl.eps, path=args.path, rw=rw, out=bt.out)
+            run_op(bt, rp, ci, pe)
         torch.cuda.synchronize()
         print("# counters run done", file=sys.stderr, flush=True)
         return
 
     # R rotating copies so that one step's inputs are not cache-resident
-    R = max(2, min(16, math.ceil(3 * MALL_BYTES / max(batch_bytes(wl, es), 1)) + 1))
+    R = max(2, min(16, math.ceil(3 * MALL_BYTES / max(batch_bytes(wl, es, args.variant), 1)) + 1))
     print(f"# {wl.name}: N={wl.num_nodes} nnz={wl.nnz}; {R} rotating batches", file=sys.stderr, flush=True)
     batches = [Batch(wl, dev, host) for _ in range(R)]
-    use_rw = args.path == "mfma" or (args.path == "auto" and wl.dtype != "f32" and wl.mode == "standard"
-                                     and not wl.has_e)
+    use_rw = args.variant == "forward" and (args.path == "mfma" or (
+        args.path == "auto" and wl.dtype != "f32" and wl.mode == "standard" and not wl.has_e))
 
     def step(i, ev=None):
         b = batches[i % R]
         if ev is not None:
             ev[0].record()
-        rp, ci, _ = b.csr(b.src, b.dst)
+        rp, ci, pe = b.csr(b.src, b.dst)
         if use_rw:
             if b.rw is None:          # row windows once per graph (they synchronize; never inside timing)
                 b.rw = gsa.gattn_build_rowwindows(rp, ci, wl.num_nodes)
         if ev is not None:
             ev[1].record()
-        gsa.gattn_forward(rp, ci, b.q, b.k, b.v, b.e, mode=wl.mode, scale=wl.scale, clip=wl.clip, eps=wl.eps,
-                          path=args.path, rw=b.rw, out=b.out)
+        run_op(b, rp, ci, pe)
         if ev is not None:
             ev[2].record()
 
@@ -262,7 +305,7 @@ def main():
     torch.cuda.synchronize()
     for b in batches:
         assert int(b.csr.status.item()) == 0, "bad graph"
-    path = gsa.gattn_forward_path(batches[0].csr.row_ptr, batches[0].csr.col_idx, batches[0].q, batches[0].k,
+    path = "gather" if args.variant == "aggregate" else gsa.gattn_forward_path(batches[0].csr.row_ptr, batches[0].csr.col_idx, batches[0].q, batches[0].k,
                                   batches[0].v, batches[0].e, mode=wl.mode, path=args.path, rw=batches[0].rw)
 
     # host enqueue rate, to size the sleep that keeps the GPU backlogged
@@ -290,10 +333,10 @@ def main():
     ms_per_step = total_ms / K
 
     nnz = wl.nnz
-    bmin = algorithmic_bytes(wl.num_nodes, nnz, wl.heads, wl.head_dim, es, wl.has_e)
+    bmin = algorithmic_bytes(wl.num_nodes, nnz, wl.heads, wl.head_dim, es, wl.has_e, args.variant)
     achieved = bmin / (fwd_ms * 1e-3) / 1e9
     pk = "mfma" if path == "mfma" else "gather"
-    tr = load_traffic(pk, args.config)
+    tr = load_traffic(pk, args.config, args.variant)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": (round(tr["hbm_bytes_per_launch"]) if tr and tr.get("hbm_bytes_per_launch") else None),
@@ -305,15 +348,18 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
            "data": "synthetic",
            "config": {"workload": wl.name, "config_index": args.config, "nodes": wl.num_nodes, "edges": nnz,
-                      "heads": wl.heads, "head_dim": wl.head_dim, "softmax": wl.mode, "edge_projection": wl.has_e,
-                      "step": "gattn_build_csr + gattn_forward", "forward_path": path,
+                      "heads": wl.heads, "head_dim": wl.head_dim,
+                      "softmax": "none (given weights)" if args.variant == "aggregate" else wl.mode,
+                      "edge_projection": wl.has_e and args.variant != "aggregate",
+                      "step": f"gattn_build_csr + {VARIANTS[args.variant]}", "variant": args.variant,
+                      "forward_path": path,
                       "rotating_batches": R},
            "roofline": roofline,
            "forward_gedges_per_s": round(nnz / (fwd_ms * 1e-3) / 1e9, 4),
            "build_csr_ms": round(build_ms, 5)}
     if not args.no_cpu:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds, args.variant)
     print(json.dumps(res), flush=True)
 
 

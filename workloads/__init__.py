@@ -44,7 +44,7 @@ from typing import Optional
 
 import numpy as np
 
-STREAM_GRAPH, STREAM_Q, STREAM_K, STREAM_V, STREAM_E, STREAM_ORDER = range(6)
+STREAM_GRAPH, STREAM_Q, STREAM_K, STREAM_V, STREAM_E, STREAM_ORDER, STREAM_W = range(7)
 
 
 def rng_for(config: int, stream: int, seed: int = 0) -> np.random.Generator:
@@ -96,6 +96,12 @@ class Workload:
             return None
         g = rng_for(self.config, STREAM_E, self.seed)
         return g.standard_normal((self.nnz, self.heads, self.head_dim), dtype=np.float32)
+
+    def w(self) -> np.ndarray:
+        """float32 positive per-edge weights [nnz, H] for the weighted
+        aggregation, lognormal(0, 1) like exponentiated scores."""
+        g = rng_for(self.config, STREAM_W, self.seed)
+        return np.exp(g.standard_normal((self.nnz, self.heads), dtype=np.float32))
 
 
 def cast(x: np.ndarray, dtype: str):
