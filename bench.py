@@ -52,8 +52,10 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = {"gather": "graph_sparse_attention_amd/csrc/forward_gather.hip",
-              "mfma": "graph_sparse_attention_amd/csrc/forward_mfma.hip"}
+KERNEL_SRC = {"gather": ["graph_sparse_attention_amd/csrc/gather_kernel.hpp",
+                         "graph_sparse_attention_amd/csrc/forward_gather.hip",
+                         "graph_sparse_attention_amd/csrc/forward_gather_split.hip"],
+              "mfma": ["graph_sparse_attention_amd/csrc/forward_mfma.hip"]}
 COPY_BYTES = 512 << 20      # calibration copy for the traffic counters
 VARIANTS = {"forward": "gattn_forward", "e_out": "gattn_forward + edge update",
             "edge_ids": "gattn_forward, E through edge ids", "aggregate": "gattn_aggregate (normalized)"}
@@ -67,6 +69,8 @@ def parse():
     p.add_argument("--config", type=int, default=2)
     p.add_argument("--path", default="auto", choices=["auto", "gather", "mfma"])
     p.add_argument("--variant", default="forward", choices=list(VARIANTS))
+    p.add_argument("--partition", default="balanced", choices=["balanced", "node"],
+                   help="gather path: edge-balanced workgroups with cut heavy rows (workspace) or equal node counts")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bound of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--counters-run", action="store_true")
@@ -75,8 +79,11 @@ def parse():
 
 
 def src_hash(path_key):
-    with open(os.path.join(ROOT, KERNEL_SRC[path_key]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for rel in KERNEL_SRC[path_key]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 # ---------------------------------------------------------------------------
@@ -100,7 +107,7 @@ def algorithmic_bytes(n, nnz, h, d, s, has_e, variant="forward"):
 
 
 class Batch:
-    def __init__(self, wl, dev, host):
+    def __init__(self, wl, dev, host, variant="forward", partition="balanced"):
         import torch
         import graph_sparse_attention_amd as gsa
         self.src = host["src"].to(dev)
@@ -112,6 +119,13 @@ class Batch:
         self.e_out = torch.empty_like(self.e) if host.get("e_out") and self.e is not None else None
         self.csr = gsa.CsrBuilder(wl.num_nodes, wl.nnz, dev)
         self.rw = None
+        self.ws = None
+        if partition == "balanced":
+            rp, ci = self.csr.row_ptr, self.csr.col_idx
+            nbytes = (gsa.gattn_aggregate_workspace(rp, ci, self.v) if variant == "aggregate" else
+                      gsa.gattn_forward_workspace(rp, ci, self.q, self.k, self.v, self.e, wl.mode,
+                                                  e_out=self.e_out is not None))
+            self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev) if nbytes else None
 
 
 def make_host_inputs(wl, variant="forward"):
@@ -174,14 +188,14 @@ def cpu_baseline(wl, host, seconds, variant="forward"):
 # counters
 # ---------------------------------------------------------------------------
 
-def counters_file(path_key, config, variant="forward"):
-    suffix = "" if variant == "forward" else f"_{variant}"
+def counters_file(path_key, config, variant="forward", partition="balanced"):
+    suffix = ("" if variant == "forward" else f"_{variant}") + ("_node" if partition == "node" and path_key == "gather" else "")
     return os.path.join(PROFILES, f"{'forward_gather' if path_key == 'gather' else 'forward_mfma'}"
                                   f"_config{config}{suffix}_counters.json")
 
 
-def load_traffic(path_key, config, variant="forward"):
-    f = counters_file(path_key, config, variant)
+def load_traffic(path_key, config, variant="forward", partition="balanced"):
+    f = counters_file(path_key, config, variant, partition)
     if not os.path.exists(f):
         return None
     d = json.load(open(f))
@@ -190,7 +204,7 @@ def load_traffic(path_key, config, variant="forward"):
     return d
 
 
-def ingest_counters(dirname, config, path_key, variant="forward"):
+def ingest_counters(dirname, config, path_key, variant="forward", partition="balanced"):
     """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the forward kernel
     and of the calibration copy; scale by the copy's bytes-per-count."""
     rows = []
@@ -215,14 +229,15 @@ def ingest_counters(dirname, config, path_key, variant="forward"):
     copy_write = res.get("copy_WRITE_SIZE")
     fr = COPY_BYTES / (copy_read * 1024.0) if copy_read else None
     fw = COPY_BYTES / (copy_write * 1024.0) if copy_write else None
-    out = {"kernel": kern, "config": config, "variant": variant, "kernel_source_sha256_16": src_hash(path_key),
+    out = {"kernel": kern, "config": config, "variant": variant, "partition": partition,
+           "kernel_source_sha256_16": src_hash(path_key),
            "fetch_kib_per_dispatch": res.get("fwd_FETCH_SIZE"), "write_kib_per_dispatch": res.get("fwd_WRITE_SIZE"),
            "copy_fetch_kib": copy_read, "copy_write_kib": copy_write, "copy_bytes_each_way": COPY_BYTES,
            "read_scale": fr, "write_scale": fw}
     if res.get("fwd_FETCH_SIZE") is not None and fr and res.get("fwd_WRITE_SIZE") is not None and fw:
         out["hbm_bytes_per_launch"] = res["fwd_FETCH_SIZE"] * 1024.0 * fr + res["fwd_WRITE_SIZE"] * 1024.0 * fw
     os.makedirs(PROFILES, exist_ok=True)
-    with open(counters_file(path_key, config, variant), "w") as fh:
+    with open(counters_file(path_key, config, variant, partition), "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out))
 
@@ -238,7 +253,7 @@ def main():
     import workloads as W
     if args.ingest_counters:
         path_key = "mfma" if args.path == "mfma" else "gather"
-        ingest_counters(args.ingest_counters, args.config, path_key, args.variant)
+        ingest_counters(args.ingest_counters, args.config, path_key, args.variant, args.partition)
         return
 
     import torch
@@ -256,11 +271,12 @@ def main():
 
     def run_op(b, rp, ci, pe):
         if args.variant == "aggregate":
-            gsa.gattn_aggregate(rp, ci, b.v, b.w, normalize=True, eps=wl.eps, out=b.out)
+            gsa.gattn_aggregate(rp, ci, b.v, b.w, normalize=True, eps=wl.eps, out=b.out, workspace=b.ws)
         else:
             gsa.gattn_forward(rp, ci, b.q, b.k, b.v, b.e, mode=wl.mode, scale=wl.scale, clip=wl.clip, eps=wl.eps,
                               path=args.path, rw=b.rw, out=b.out,
-                              edge_ids=pe if args.variant == "edge_ids" else None, e_out=b.e_out)
+                              edge_ids=pe if args.variant == "edge_ids" else None, e_out=b.e_out,
+                              workspace=b.ws)
 
     if args.counters_run:
         a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -269,7 +285,7 @@ def main():
         torch.cuda.synchronize()
         b.copy_(a)                      # calibration: COPY_BYTES read + COPY_BYTES written (runtime copyBuffer kernel)
         torch.cuda.synchronize()
-        bt = Batch(wl, dev, host)
+        bt = Batch(wl, dev, host, args.variant, args.partition)
         rp, ci, pe = bt.csr(bt.src, bt.dst)
         bt.rw = gsa.gattn_build_rowwindows(rp, ci, wl.num_nodes) if args.path == "mfma" else None
         for _ in range(5):
@@ -281,7 +297,7 @@ def main():
     # R rotating copies so that one step's inputs are not cache-resident
     R = max(2, min(16, math.ceil(3 * MALL_BYTES / max(batch_bytes(wl, es, args.variant), 1)) + 1))
     print(f"# {wl.name}: N={wl.num_nodes} nnz={wl.nnz}; {R} rotating batches", file=sys.stderr, flush=True)
-    batches = [Batch(wl, dev, host) for _ in range(R)]
+    batches = [Batch(wl, dev, host, args.variant, args.partition) for _ in range(R)]
     use_rw = args.variant == "forward" and (args.path == "mfma" or (
         args.path == "auto" and wl.dtype != "f32" and wl.mode == "standard" and not wl.has_e))
 
@@ -336,7 +352,7 @@ def main():
     bmin = algorithmic_bytes(wl.num_nodes, nnz, wl.heads, wl.head_dim, es, wl.has_e, args.variant)
     achieved = bmin / (fwd_ms * 1e-3) / 1e9
     pk = "mfma" if path == "mfma" else "gather"
-    tr = load_traffic(pk, args.config, args.variant)
+    tr = load_traffic(pk, args.config, args.variant, args.partition)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": (round(tr["hbm_bytes_per_launch"]) if tr and tr.get("hbm_bytes_per_launch") else None),
@@ -352,6 +368,7 @@ def main():
                       "softmax": "none (given weights)" if args.variant == "aggregate" else wl.mode,
                       "edge_projection": wl.has_e and args.variant != "aggregate",
                       "step": f"gattn_build_csr + {VARIANTS[args.variant]}", "variant": args.variant,
+                      "partition": args.partition if path == "gather" else None,
                       "forward_path": path,
                       "rotating_batches": R},
            "roofline": roofline,

@@ -10,7 +10,7 @@ current stream.  Names follow the C ABI in ``include/gattn.h``:
     gattn_forward_path(...)                         -> "gather" | "mfma"
     gattn_aggregate(row_ptr, col_idx, x, w, ...)    -> out [N, H, D]
 
-Importing this module raises if ``libgattn.so`` is missing: there is no
+Every call raises if ``libgattn.so`` is missing or stale: there is no
 fallback implementation.  Build it with ``python -m
 graph_sparse_attention_amd.build``.
 """
@@ -59,7 +59,8 @@ class _ForwardArgs(ctypes.Structure):
                 ("out", ctypes.c_void_p), ("dtype", ctypes.c_int), ("mode", ctypes.c_int),
                 ("scale", ctypes.c_float), ("clip_lo", ctypes.c_float), ("clip_hi", ctypes.c_float),
                 ("eps", ctypes.c_float), ("path", ctypes.c_int), ("rw", ctypes.POINTER(_RowWindows)),
-                ("flags", ctypes.c_uint32), ("edge_ids", ctypes.c_void_p), ("e_out", ctypes.c_void_p)]
+                ("flags", ctypes.c_uint32), ("edge_ids", ctypes.c_void_p), ("e_out", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class _AggregateArgs(ctypes.Structure):
@@ -68,7 +69,20 @@ class _AggregateArgs(ctypes.Structure):
                 ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p), ("x", ctypes.c_void_p),
                 ("w", ctypes.c_void_p), ("edge_ids", ctypes.c_void_p), ("out", ctypes.c_void_p),
                 ("dtype", ctypes.c_int), ("normalize", ctypes.c_int32), ("eps", ctypes.c_float),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class _Unloaded:
+    """Stands in for a library that is missing, stale or unloadable: every use
+    raises, so nothing can run without the HIP kernels (and the build script
+    can still be imported to rebuild it)."""
+
+    def __init__(self, err: Exception):
+        self._err = err
+
+    def __getattr__(self, name):
+        raise ImportError(f"libgattn.so is not usable ({self._err}); "
+                          "run `python -m graph_sparse_attention_amd.build`")
 
 
 def _load():
@@ -88,13 +102,19 @@ def _load():
     L.gattn_forward.argtypes = [ctypes.POINTER(_ForwardArgs), vp]
     L.gattn_forward_path.argtypes = [ctypes.POINTER(_ForwardArgs), ctypes.POINTER(ctypes.c_int)]
     L.gattn_aggregate.argtypes = [ctypes.POINTER(_AggregateArgs), vp]
+    L.gattn_forward_workspace.argtypes = [ctypes.POINTER(_ForwardArgs), sz]
+    L.gattn_aggregate_workspace.argtypes = [ctypes.POINTER(_AggregateArgs), sz]
     for f in (L.gattn_build_csr_workspace, L.gattn_build_csr, L.gattn_build_rowwindows_workspace,
-              L.gattn_build_rowwindows, L.gattn_forward, L.gattn_forward_path, L.gattn_aggregate):
+              L.gattn_build_rowwindows, L.gattn_forward, L.gattn_forward_path, L.gattn_aggregate,
+              L.gattn_forward_workspace, L.gattn_aggregate_workspace):
         f.restype = st
     return L
 
 
-_lib = _load()
+try:
+    _lib = _load()
+except (ImportError, OSError, AttributeError) as _e:   # missing file, failed dlopen, missing symbol
+    _lib = _Unloaded(_e)
 
 
 def gattn_abi_version() -> int:
@@ -240,6 +260,49 @@ def _forward_args(row_ptr, col_idx, q, k, v, e, out, mode, scale, clip, eps, pat
     return a, keep
 
 
+def _attach_workspace(a, query, workspace, device, what):
+    """workspace: True -> allocate the queried size, a uint8 GPU tensor -> use
+    it, None / False -> none (node partition)."""
+    if workspace is None or workspace is False:
+        return None
+    nbytes = ctypes.c_size_t()
+    _check(query(ctypes.byref(a), ctypes.byref(nbytes)), what)
+    if nbytes.value == 0:
+        return None
+    if workspace is True:
+        workspace = torch.empty(nbytes.value, dtype=torch.uint8, device=device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_cuda or workspace.numel() < nbytes.value:
+        raise ValueError(f"workspace must be a uint8 GPU tensor of at least {nbytes.value} bytes")
+    a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    return workspace
+
+
+def gattn_forward_workspace(row_ptr, col_idx, q, k, v, e=None, mode="standard", e_out=False) -> int:
+    """Bytes of the balanced-partition workspace for these tensors."""
+    a, keep = _forward_args(row_ptr, col_idx, q, k, v, e, None, mode, None, (-5.0, 5.0), 1e-6, "gather", None,
+                            False, None, None)
+    if e_out:
+        a.e_out = 256        # never dereferenced: only its presence sets the size
+    nbytes = ctypes.c_size_t()
+    _check(_lib.gattn_forward_workspace(ctypes.byref(a), ctypes.byref(nbytes)), "gattn_forward_workspace")
+    del keep
+    return nbytes.value
+
+
+def gattn_aggregate_workspace(row_ptr, col_idx, x) -> int:
+    """Bytes of the balanced-partition workspace of gattn_aggregate for these tensors."""
+    N, H, D = x.shape
+    a = _AggregateArgs()
+    a.struct_size = ctypes.sizeof(_AggregateArgs)
+    a.num_nodes, a.num_heads, a.head_dim, a.nnz = N, H, D, col_idx.numel()
+    a.row_ptr, a.col_idx, a.x, a.out = row_ptr.data_ptr(), col_idx.data_ptr(), x.data_ptr(), None
+    a.w = 256            # never dereferenced
+    a.dtype = _DTYPES[x.dtype]
+    nbytes = ctypes.c_size_t()
+    _check(_lib.gattn_aggregate_workspace(ctypes.byref(a), ctypes.byref(nbytes)), "gattn_aggregate_workspace")
+    return nbytes.value
+
+
 def _check_node_tensor(t, name, like):
     if t.dtype != like.dtype or t.shape != like.shape or not t.is_contiguous() or t.device != like.device:
         raise ValueError(f"{name} must match q in dtype, shape and device and be contiguous")
@@ -249,11 +312,13 @@ def gattn_forward(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch.Tensor,
                   e: Optional[torch.Tensor] = None, mode: str = "standard", scale: Optional[float] = None,
                   clip=(-5.0, 5.0), eps: float = 1e-6, path: str = "auto", rw: Optional[RowWindows] = None,
                   out: Optional[torch.Tensor] = None, validate: bool = False,
-                  edge_ids: Optional[torch.Tensor] = None, e_out=None):
+                  edge_ids: Optional[torch.Tensor] = None, e_out=None, workspace=True):
     """Fused SDDMM -> softmax -> SpMM over the CSR; q/k/v [N, H, D]; e
     [nnz, H, D] by CSR position (or row edge_ids[p] for position p) or None.
     Returns out [N, H, D]; with e_out (True, or an [nnz, H, D] tensor) the
-    clipped mode also writes the per-edge update and returns (out, e_out)."""
+    clipped mode also writes the per-edge update and returns (out, e_out).
+    workspace: True (default) allocates the balanced-partition workspace, a
+    uint8 tensor supplies it, None runs the node partition."""
     row_ptr, col_idx = _i32(row_ptr, "row_ptr"), _i32(col_idx, "col_idx")
     if q.dim() != 3 or not q.is_contiguous() or not q.is_cuda:
         raise ValueError("q must be a contiguous [N, H, D] GPU tensor")
@@ -278,8 +343,9 @@ def gattn_forward(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch.Tensor,
         _check_node_tensor(out, "out", q)
     a, keep = _forward_args(row_ptr, col_idx, q, k, v, e, out, mode, scale, clip, eps, path, rw, validate,
                             edge_ids, e_out if want_e_out else None)
+    ws = _attach_workspace(a, _lib.gattn_forward_workspace, workspace, q.device, "gattn_forward_workspace")
     _check(_lib.gattn_forward(ctypes.byref(a), _stream(q.device)), "gattn_forward")
-    del keep
+    del keep, ws
     return (out, e_out) if want_e_out else out
 
 
@@ -294,10 +360,10 @@ def gattn_forward_path(row_ptr, col_idx, q, k, v, e=None, mode="standard", path=
 
 def gattn_aggregate(row_ptr: torch.Tensor, col_idx: torch.Tensor, x: torch.Tensor, w: torch.Tensor,
                     normalize: bool = False, eps: float = 1e-6, edge_ids: Optional[torch.Tensor] = None,
-                    out: Optional[torch.Tensor] = None, validate: bool = False) -> torch.Tensor:
+                    out: Optional[torch.Tensor] = None, validate: bool = False, workspace=True) -> torch.Tensor:
     """Weighted aggregation over the CSR: x [N, H, D], w [nnz, H] fp32 (row
     edge_ids[p] for position p when given); out[i] = sum_p w x[src], divided
-    by (sum_p w + eps) when normalize."""
+    by (sum_p w + eps) when normalize.  workspace as in gattn_forward."""
     row_ptr, col_idx = _i32(row_ptr, "row_ptr"), _i32(col_idx, "col_idx")
     if x.dim() != 3 or not x.is_contiguous() or not x.is_cuda or x.dtype not in _DTYPES:
         raise ValueError("x must be a contiguous [N, H, D] GPU tensor")
@@ -323,9 +389,12 @@ def gattn_aggregate(row_ptr: torch.Tensor, col_idx: torch.Tensor, x: torch.Tenso
     a.normalize = 1 if normalize else 0
     a.eps = eps
     a.flags = GATTN_FLAG_VALIDATE if validate else 0
+    ws = _attach_workspace(a, _lib.gattn_aggregate_workspace, workspace, x.device, "gattn_aggregate_workspace")
     _check(_lib.gattn_aggregate(ctypes.byref(a), _stream(x.device)), "gattn_aggregate")
+    del ws
     return out
 
 
 __all__ = ["gattn_build_csr", "gattn_build_rowwindows", "gattn_forward", "gattn_forward_path", "gattn_aggregate",
+           "gattn_forward_workspace", "gattn_aggregate_workspace",
            "gattn_status_string", "gattn_abi_version", "CsrBuilder", "RowWindows", "GattnError", "LIB_PATH"]

@@ -13,8 +13,8 @@
 using namespace gattn;
 
 // the Python binding mirrors these layouts with ctypes
-static_assert(sizeof(gattn_forward_args) == 144, "gattn_forward_args layout");
-static_assert(sizeof(gattn_aggregate_args) == 88, "gattn_aggregate_args layout");
+static_assert(sizeof(gattn_forward_args) == 160, "gattn_forward_args layout");
+static_assert(sizeof(gattn_aggregate_args) == 104, "gattn_aggregate_args layout");
 static_assert(sizeof(gattn_rowwindows) == 40, "gattn_rowwindows layout");
 
 namespace {
@@ -69,10 +69,21 @@ gattn_status check_forward(const gattn_forward_args* a, bool launch) {
         overlap(a->e_out, edge_bytes, a->col_idx, ib) || overlap(a->e_out, edge_bytes, a->edge_ids, ib))
       return GATTN_ERR_INVALID_VALUE;
   }
+  if (a->workspace) {
+    const size_t wb = a->workspace_bytes;
+    if (!aligned(a->workspace, 256)) return GATTN_ERR_INVALID_VALUE;
+    if (overlap(a->workspace, wb, a->q, node_bytes) || overlap(a->workspace, wb, a->k, node_bytes) ||
+        overlap(a->workspace, wb, a->v, node_bytes) || overlap(a->workspace, wb, a->e, edge_bytes) ||
+        overlap(a->workspace, wb, a->out, node_bytes) || overlap(a->workspace, wb, a->e_out, edge_bytes) ||
+        overlap(a->workspace, wb, a->row_ptr, 4 * ((size_t)a->num_nodes + 1)) ||
+        overlap(a->workspace, wb, a->col_idx, (size_t)a->nnz * 4) ||
+        overlap(a->workspace, wb, a->edge_ids, (size_t)a->nnz * 4))
+      return GATTN_ERR_INVALID_VALUE;
+  }
   return GATTN_OK;
 }
 
-gattn_status check_aggregate(const gattn_aggregate_args* a) {
+gattn_status check_aggregate(const gattn_aggregate_args* a, bool launch) {
   if (!a || a->struct_size != sizeof(gattn_aggregate_args)) return GATTN_ERR_INVALID_VALUE;
   if (a->num_nodes < 0 || a->num_heads < 1 || a->nnz < 0 || a->nnz > INT32_MAX) return GATTN_ERR_INVALID_VALUE;
   if (a->dtype != GATTN_F32 && a->dtype != GATTN_F16 && a->dtype != GATTN_BF16) return GATTN_ERR_INVALID_VALUE;
@@ -82,7 +93,7 @@ gattn_status check_aggregate(const gattn_aggregate_args* a) {
   if (a->head_dim != 16 && a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128) return GATTN_ERR_UNSUPPORTED;
   if ((int64_t)a->num_heads * a->head_dim > (int64_t)1 << 20) return GATTN_ERR_UNSUPPORTED;
   if (a->num_nodes == 0) return GATTN_OK;
-  if (!a->row_ptr || !a->x || !a->out) return GATTN_ERR_INVALID_VALUE;
+  if (!a->row_ptr || !a->x || (launch && !a->out)) return GATTN_ERR_INVALID_VALUE;
   if (a->nnz > 0 && (!a->col_idx || !a->w)) return GATTN_ERR_INVALID_VALUE;
   if (!aligned(a->row_ptr, 4) || !aligned(a->col_idx, 4) || !aligned(a->edge_ids, 4) || !aligned(a->w, 4))
     return GATTN_ERR_INVALID_VALUE;
@@ -94,6 +105,16 @@ gattn_status check_aggregate(const gattn_aggregate_args* a) {
       overlap(a->out, node_bytes, a->col_idx, (size_t)a->nnz * 4) ||
       overlap(a->out, node_bytes, a->edge_ids, (size_t)a->nnz * 4))
     return GATTN_ERR_INVALID_VALUE;
+  if (a->workspace) {
+    const size_t wb = a->workspace_bytes;
+    if (!aligned(a->workspace, 256)) return GATTN_ERR_INVALID_VALUE;
+    if (overlap(a->workspace, wb, a->x, node_bytes) || overlap(a->workspace, wb, a->out, node_bytes) ||
+        overlap(a->workspace, wb, a->w, (size_t)a->nnz * a->num_heads * 4) ||
+        overlap(a->workspace, wb, a->row_ptr, 4 * ((size_t)a->num_nodes + 1)) ||
+        overlap(a->workspace, wb, a->col_idx, (size_t)a->nnz * 4) ||
+        overlap(a->workspace, wb, a->edge_ids, (size_t)a->nnz * 4))
+      return GATTN_ERR_INVALID_VALUE;
+  }
   return GATTN_OK;
 }
 
@@ -254,6 +275,30 @@ gattn_status gattn_forward_path(const gattn_forward_args* args, gattn_path* path
   return resolve(args, path);
 }
 
+gattn_status gattn_forward_workspace(const gattn_forward_args* args, size_t* bytes) {
+  try {
+    if (!bytes) return GATTN_ERR_INVALID_VALUE;
+    gattn_status st = check_forward(args, false);
+    if (st != GATTN_OK) return st;
+    *bytes = forward_gather_workspace_bytes(*args);
+    return GATTN_OK;
+  } catch (...) {
+    return GATTN_ERR_HIP;
+  }
+}
+
+gattn_status gattn_aggregate_workspace(const gattn_aggregate_args* args, size_t* bytes) {
+  try {
+    if (!bytes) return GATTN_ERR_INVALID_VALUE;
+    gattn_status st = check_aggregate(args, false);
+    if (st != GATTN_OK) return st;
+    *bytes = aggregate_workspace_bytes(*args);
+    return GATTN_OK;
+  } catch (...) {
+    return GATTN_ERR_HIP;
+  }
+}
+
 gattn_status gattn_forward(const gattn_forward_args* args, hipStream_t stream) {
   try {
     gattn_status st = check_forward(args, true);
@@ -268,6 +313,8 @@ gattn_status gattn_forward(const gattn_forward_args* args, hipStream_t stream) {
         return st;
     }
     if (path == GATTN_PATH_MFMA) return from_hip(launch_forward_mfma(*args, stream));
+    if (args->workspace && args->workspace_bytes < forward_gather_workspace_bytes(*args))
+      return GATTN_ERR_BUFFER_TOO_SMALL;
     return from_hip(launch_forward_gather(*args, stream));
   } catch (...) {
     return GATTN_ERR_HIP;
@@ -276,7 +323,7 @@ gattn_status gattn_forward(const gattn_forward_args* args, hipStream_t stream) {
 
 gattn_status gattn_aggregate(const gattn_aggregate_args* args, hipStream_t stream) {
   try {
-    gattn_status st = check_aggregate(args);
+    gattn_status st = check_aggregate(args, true);
     if (st != GATTN_OK) return st;
     if (args->num_nodes == 0) return GATTN_OK;
     if (args->flags & GATTN_FLAG_VALIDATE) {
@@ -284,6 +331,7 @@ gattn_status gattn_aggregate(const gattn_aggregate_args* args, hipStream_t strea
                                stream)) != GATTN_OK)
         return st;
     }
+    if (args->workspace && args->workspace_bytes < aggregate_workspace_bytes(*args)) return GATTN_ERR_BUFFER_TOO_SMALL;
     return from_hip(launch_aggregate_gather(*args, stream));
   } catch (...) {
     return GATTN_ERR_HIP;

@@ -1,0 +1,651 @@
+// gather_kernel.hpp -- wave64 gather kernel of the fused graph attention
+// (included by forward_gather.hip, which instantiates the node partition,
+// and forward_gather_split.hip, which instantiates the balanced one).
+//
+// What it computes (gattn-triton article, "Background" and "Fusing the full
+// graph attention"; Fused3S abstract): for every destination i and head h,
+// a logit per in-edge from q_i and k_j (times e_ij when an edge projection
+// is given), a softmax over the in-edges of i -- standard max-subtracted, or
+// the RTMScore form exp(clip) / (sum + eps) -- and o_i = sum_j alpha_ij v_j.
+// No per-edge tensor is written, except the RTMScore edge update when asked
+// for (the article's fused kernel stores clip(scale q k) * e per edge).
+// The same kernel, without logits, is the weighted CSR aggregation of the
+// POPCORNBENCH problem and of the article's scatter add (third mode below).
+// Per-edge rows (E, the edge update, aggregation weights) are addressed by
+// CSR position, or through an edge-id map (the article's CSC edge ids).
+//
+// Mapping on CDNA4.
+//  * A "slot" is a group of G lanes (G = 2..64, a power of two) that holds one
+//    edge's [HB heads x D] slice of a K / V / E row, 16 bytes per lane, so a
+//    slot's loads are one contiguous, coalesced run.  A wave holds 64/G slots,
+//    a 256-thread workgroup NS = 4*64/G slots.  The logit of a head is summed
+//    over its D/VEC lanes with DPP inside a 16-lane row.
+//  * A workgroup owns a contiguous range of destinations (node-parallel as in
+//    the article's one-program-per-node kernels and Fused3S Figure 2, top) for
+//    one block of heads.  It first stages the destinations' row pointers and
+//    Q rows in LDS (one coalesced pass).  Its edges are then cut into NS equal
+//    contiguous pieces (a merge path over the CSR): each slot walks its piece
+//    U edges at a time, prefetching the next piece of column indices (and E
+//    rows) while it computes, and keeps the online-softmax state (m, l) and
+//    the fp32 accumulator in registers.  A destination that is cut by a piece
+//    boundary leaves partial (m, l, acc) records in LDS; the slot holding its
+//    last edge merges them in slot order.  Deterministic, no atomics.
+//  * Consecutive workgroups are mapped onto one XCD so that destinations of
+//    one batched graph, whose sources are nearby, share an L2.
+//  * With a workspace, workgroups instead take equal ranges of the merged
+//    sequence of row ends and edges (a merge path over the whole CSR), found
+//    by a 64-lane search of row_ptr at the start.  A light row belongs whole to
+//    the workgroup holding its first item; a heavy row is cut at the range
+//    boundaries (edge-parallel parts, Fused3S Figure 2's node- vs edge-parallel
+//    split).  Each part leaves its (m, l, acc) in the workspace and raises a
+//    flag tagged with this launch's token; a part that then finds every flag of
+//    the row raised merges the parts in order and writes the row.  Several
+//    parts may merge; they write identical bits.  No counter needs clearing,
+//    and no cache flush is needed: the parts and flags are written and read
+//    with device-coherent (agent-scope) accesses, each wait ordering them.
+#pragma once
+
+#include <algorithm>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+#ifndef GATTN_GATHER_Q_LDS_BYTES
+#define GATTN_GATHER_Q_LDS_BYTES 12288  // Q rows staged per workgroup
+#endif
+#ifndef GATTN_GATHER_EDGES_PER_SLOT
+#define GATTN_GATHER_EDGES_PER_SLOT 3   // target edges per slot, in units of U
+#endif
+#ifndef GATTN_GATHER_U
+#define GATTN_GATHER_U 8                // edges per step without an edge tensor
+#endif
+#ifndef GATTN_GATHER_U_E
+#define GATTN_GATHER_U_E 4              // edges per step with an edge tensor
+#endif
+#ifndef GATTN_GATHER_E_STREAMING
+#define GATTN_GATHER_E_STREAMING 1      // non-temporal loads for the edge tensor
+#endif
+#ifndef GATTN_XCD_REMAP
+#define GATTN_XCD_REMAP 1
+#endif
+
+namespace gattn {
+
+constexpr int kGatherThreads = 256;
+constexpr int kMaxNodesPerWg = 1024;
+constexpr int kQLdsBytes = GATTN_GATHER_Q_LDS_BYTES;
+constexpr int kModeAggregate = 2;  // given per-edge weights instead of logits and softmax
+
+struct GatherArgs {
+  const int32_t* __restrict__ row_ptr;
+  const int32_t* __restrict__ col_idx;
+  const uint8_t* __restrict__ q;
+  const uint8_t* __restrict__ k;
+  const uint8_t* __restrict__ v;
+  const uint8_t* __restrict__ e;
+  uint8_t* __restrict__ out;
+  int64_t nnz;
+  int32_t n, H, HB, log2G, npw;
+  float scale;  // standard: scale * log2(e); clipped: scale
+  float lo, hi, eps;
+  const int32_t* __restrict__ ids;  // nullable: row of e / e_out / w for CSR position p
+  uint8_t* __restrict__ e_out;      // clipped mode with e: the per-edge update
+  const float* __restrict__ w;      // aggregate mode: [nnz, H] weights
+  int32_t normalize;                // aggregate mode: divide by (sum of w + eps)
+  // balanced partition with cut heavy rows (ws_flags != nullptr)
+  uint64_t* ws_flags;               // [2][head blocks][B] launch tokens (kind 0: first row, 1: last row)
+  float* ws_ml;                     // [2][head blocks][B][G][2] partial m, l
+  float* ws_acc;                    // [2][head blocks][B][G][VEC] partial accumulators
+  int64_t items_per_wg;             // C: width of a workgroup's range of (row ends + edges)
+  int64_t total_items;              // N + nnz
+  int32_t light_max;                // rows with deg + 1 <= light_max are never cut
+  int32_t num_wg;                   // B: workgroups per head block
+  uint64_t token;                   // this launch's flag value
+};
+
+// First item of row r in the merged sequence (row r's edges, then its end).
+__device__ __forceinline__ int64_t first_item(const GatherArgs& a, int64_t r) {
+  return r + min(max(a.row_ptr[r], 0), (int)a.nnz);
+}
+
+struct Cut {
+  int row, edge;
+  int cont;  // the range starts inside `row`: its edges before `edge` belong to earlier workgroups
+};
+
+// Start of the range that begins at item x, computed by one whole wave: r0 is
+// the last row with first_item(r0) <= x, found with a 64-position window
+// around the proportional guess (exact for uniform degrees), then a 64-way
+// search.  A light row straddling x was taken by the workgroup holding its
+// first item, so the range starts at the next row; a heavy row is cut at x.
+__device__ inline Cut locate(const GatherArgs& a, int64_t x, int lane) {
+  const int n = a.n, nnz = (int)a.nnz;
+  if (x >= a.total_items) return Cut{n, nnz, 0};
+  int64_t lo = 0, hi = n;
+  {
+    const int64_t g = min(max(x * n / a.total_items - 32, (int64_t)0), max((int64_t)n - 63, (int64_t)0));
+    const int64_t pos = min(g + lane, (int64_t)n);
+    const int k = __popcll(__ballot(first_item(a, pos) <= x));
+    if (k == 0) hi = max(g - 1, (int64_t)0);
+    else if (k == 64) lo = g + 63;
+    else lo = hi = g + k - 1;
+  }
+  while (hi > lo) {
+    const int64_t step = (hi - lo + 63) / 64;
+    const int64_t pos = lo + (int64_t)(lane + 1) * step;
+    const int k = __popcll(__ballot(pos <= hi && first_item(a, pos) <= x));
+    lo += k * step;
+    hi = min(hi, lo + step - 1);
+  }
+  const int r0 = (int)lo;
+  if (r0 >= n) return Cut{n, nnz, 0};
+  const int rs = min(max(a.row_ptr[r0], 0), nnz), re = min(max(a.row_ptr[r0 + 1], 0), nnz);
+  if (r0 + (int64_t)rs == x) return Cut{r0, rs, 0};
+  const int64_t e = x - r0;
+  if (re - rs + 1 > a.light_max && e > rs && e < re) return Cut{r0, (int)e, 1};
+  return Cut{r0 + 1, re, 0};
+}
+
+template <typename T, int D, int MODE, bool HAS_E, bool EOUT>
+struct EdgeMath {
+  static constexpr int VEC = Elem<T>::kVec;
+  static constexpr int LPH = D / VEC;
+
+  // one edge: logit, online softmax update, accumulate v (aggregate mode: the
+  // given weight wt instead of a softmax weight); EOUT: xo = the edge update
+  static __device__ __forceinline__ void step(const GatherArgs& a, const float* qf, u32x4 kr, u32x4 er,
+                                              u32x4 vr, float wt, float& m, float& l, float* acc, u32x4& xo) {
+    float kf[VEC], vf[VEC], ef[VEC];
+    Conv<T>::widen(kr, kf);
+    Conv<T>::widen(vr, vf);
+    if constexpr (HAS_E) Conv<T>::widen(er, ef);
+    float s = 0.f;
+    if constexpr (MODE == GATTN_SOFTMAX_STANDARD) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) s += HAS_E ? qf[i] * kf[i] * ef[i] : qf[i] * kf[i];
+      s = group_sum<LPH>(s);
+      const float lg = s * a.scale;  // log2 domain
+      const float mn = fmaxf(m, lg);
+      // exp2(0) is exactly 1: keep the running max's own weight and an unchanged
+      // max's rescale exact (the hardware exp2 is a 1-ulp approximation)
+      const float corr = m == mn ? 1.f : fast_exp2(m - mn);
+      const float p = lg == mn ? 1.f : fast_exp2(lg - mn);
+      l = l * corr + p;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] = acc[i] * corr + p * vf[i];
+      m = mn;
+    } else if constexpr (MODE == kModeAggregate) {
+      l += wt;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] += wt * vf[i];
+    } else {
+      float xs[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        float t = fminf(fmaxf(a.scale * qf[i] * kf[i], a.lo), a.hi);
+        xs[i] = HAS_E ? t * ef[i] : t;
+        s += xs[i];
+      }
+      if constexpr (EOUT) xo = Conv<T>::narrow(xs);
+      s = group_sum<LPH>(s);
+      const float lg = fminf(fmaxf(s, a.lo), a.hi);
+      const float p = fast_exp2(lg * kLog2e);
+      l += p;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] += p * vf[i];
+    }
+  }
+
+  static __device__ __forceinline__ void store(const GatherArgs& a, uint8_t* dst, float l, const float* acc) {
+    float inv;
+    if constexpr (MODE == GATTN_SOFTMAX_STANDARD) inv = 1.0f / l;
+    else if constexpr (MODE == kModeAggregate) inv = a.normalize ? 1.0f / (l + a.eps) : 1.0f;
+    else inv = 1.0f / (l + a.eps);
+    float o[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) o[i] = acc[i] * inv;
+    st16(dst, Conv<T>::narrow(o));
+  }
+
+  // fold partial state (m2, l2, acc2) into (m, l, acc), in that order
+  static __device__ __forceinline__ void fold(float& m, float& l, float* acc, float m2, float l2, const float* acc2) {
+    if constexpr (MODE == GATTN_SOFTMAX_STANDARD) {
+      const float mn = fmaxf(m, m2);
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      const float c1 = fast_exp2(m - mu), c2 = fast_exp2(m2 - mu);
+      l = l * c1 + l2 * c2;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] = acc[i] * c1 + acc2[i] * c2;
+      m = mn;
+    } else {
+      l += l2;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] += acc2[i];
+    }
+  }
+};
+
+template <typename T, int D, int MODE, bool HAS_E, bool EOUT, int U, bool SPLIT>
+__global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
+  using M = EdgeMath<T, D, MODE, HAS_E, EOUT>;
+  constexpr int VEC = Elem<T>::kVec;
+  constexpr int LPH = D / VEC;
+  constexpr int ESZ = sizeof(T);
+  constexpr bool AGG = MODE == kModeAggregate;
+  constexpr bool ROWS = HAS_E || AGG;  // per-edge rows are read
+
+  __shared__ int32_t s_rp[kMaxNodesPerWg + 1];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[AGG ? 16 : kQLdsBytes];
+  // partial records: [0] first destination of a piece (started in an earlier
+  // piece), [1] last destination of a piece (continues into a later one)
+  __shared__ float s_pm[2][kGatherThreads];
+  __shared__ float s_pl[2][kGatherThreads];
+  __shared__ float s_pacc[2][kGatherThreads * VEC];
+  __shared__ int32_t s_cut[6];  // (row, edge, cont) where the range starts and where it ends
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = 1 << a.log2G;
+  const int spw = 64 >> a.log2G;
+  const int NS = 4 * spw;
+  const int slot = wave * spw + (lane >> a.log2G);
+  const int lig = lane & (G - 1);
+  const int rec = slot * G + lig;
+  const int hh = lig / LPH, dch = lig % LPH;
+  const int hb = blockIdx.y;
+  const int head = hb * a.HB + hh;
+  const bool active = hh < a.HB && head < a.H;
+  const int64_t rowstride = (int64_t)a.H * D;
+  const int64_t eoff = (int64_t)head * D + dch * VEC;
+  const int nmax = a.n - 1;
+  const int heads_here = min(a.HB, a.H - hb * a.HB);
+  const int chunks = heads_here * LPH;                 // 16-byte chunks of this head block per node
+  const int qrow = a.HB * D * ESZ;                     // LDS bytes per staged Q row
+
+  const int blk = GATTN_XCD_REMAP ? (int)xcd_contiguous_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  const int nnz_i = (int)a.nnz;
+  constexpr bool split = SPLIT;  // balanced partition (ranges of row ends + edges, cut heavy rows)
+  int n0, nn;
+  bool cont_first = false, cont_last = false;
+  if constexpr (split) {
+    if (wave < 2) {
+      const Cut c = locate(a, (int64_t)(blk + wave) * a.items_per_wg, lane);
+      if (lane == 0) {
+        s_cut[wave * 3] = c.row;
+        s_cut[wave * 3 + 1] = c.edge;
+        s_cut[wave * 3 + 2] = c.cont;
+      }
+    }
+    __syncthreads();
+    // workgroup-uniform: keep them in scalar registers
+    n0 = __builtin_amdgcn_readfirstlane(s_cut[0]);
+    cont_first = __builtin_amdgcn_readfirstlane(s_cut[2]) != 0;
+    cont_last = __builtin_amdgcn_readfirstlane(s_cut[5]) != 0;
+    const int row_end = cont_last ? __builtin_amdgcn_readfirstlane(s_cut[3]) : __builtin_amdgcn_readfirstlane(s_cut[3]) - 1;
+    nn = max(0, min(row_end - n0 + 1, kMaxNodesPerWg));
+  } else {
+    n0 = blk * a.npw;
+    nn = min(a.npw, a.n - n0);
+  }
+  const int qcap = AGG ? 0 : kQLdsBytes / qrow;  // rows whose Q is staged in LDS
+
+  // ---- phase 0: row pointers and Q rows into LDS (one coalesced pass); a
+  // range that starts or ends inside a row starts or ends at the cut edge
+  for (int t = tid; t <= nn; t += kGatherThreads) {
+    int v = min(max(a.row_ptr[n0 + t], 0), nnz_i);
+    if (split && t == nn) v = s_cut[4];
+    if (split && t == 0) v = s_cut[1];
+    s_rp[t] = v;
+  }
+  if constexpr (!AGG) {
+    for (int t = tid; t < min(nn, qcap) * chunks; t += kGatherThreads) {
+      const int li = t / chunks, c = t - li * chunks;
+      *reinterpret_cast<u32x4*>(s_q + li * qrow + c * 16) =
+          ld16(a.q + ((int64_t)(n0 + li) * rowstride + (int64_t)hb * a.HB * D + c * VEC) * ESZ);
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < nn * chunks; t += kGatherThreads) {
+    const int li = t / chunks, c = t - li * chunks;
+    if (s_rp[li + 1] - s_rp[li] <= 0)
+      st16(a.out + ((int64_t)(n0 + li) * rowstride + (int64_t)hb * a.HB * D + c * VEC) * ESZ, u32x4{0u, 0u, 0u, 0u});
+  }
+
+  // ---- phase 1: equal contiguous pieces of the workgroup's edges
+  const int E0 = __builtin_amdgcn_readfirstlane(s_rp[0]);
+  const int E1 = max(E0, __builtin_amdgcn_readfirstlane(s_rp[nn]));
+  const int C = max((E1 - E0 + NS - 1) / NS, 1);
+  const int ps = min(E0 + slot * C, E1);
+  const int pe = min(ps + C, E1);
+  int node = 0, nstart = 0, nend = 0;
+  bool first_rec = false;   // this slot holds a record [0]
+  int rec0_node = -1;
+  if (ps < pe) {
+    int lo = 0, hi = nn - 1;  // last local node with s_rp[node] <= ps
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_rp[mid] <= ps) lo = mid; else hi = mid - 1;
+    }
+    node = lo;
+    nstart = s_rp[node];
+    nend = s_rp[node + 1];
+    while (nend <= ps && node < nn - 1) {  // only reachable for malformed pointers
+      ++node;
+      nstart = nend;
+      nend = s_rp[node + 1];
+    }
+  }
+  float m = -INFINITY, l = 0.f, acc[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+  float qf[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) qf[i] = 0.f;
+  auto load_q = [&](int nd) {
+    if constexpr (!AGG) {
+      if (!active) return;
+      const u32x4 qv = nd < qcap ? *reinterpret_cast<const u32x4*>(s_q + nd * qrow + lig * 16)
+                                 : ld16(a.q + ((int64_t)(n0 + nd) * rowstride + eoff) * ESZ);
+      Conv<T>::widen(qv, qf);
+    }
+  };
+  if (ps < pe) load_q(node);
+
+  // row of the per-edge tensors for CSR position p (clamped like the sources)
+  auto edge_row = [&](int p) -> int { return a.ids ? min(max(a.ids[p], 0), nnz_i - 1) : p; };
+  auto load_e = [&](int row) -> u32x4 {
+    const uint8_t* ptr = a.e + ((int64_t)row * rowstride + eoff) * ESZ;
+    return GATTN_GATHER_E_STREAMING ? ld16_stream(ptr) : ld16(ptr);
+  };
+
+  // a row cut across workgroups always leaves records (merged in phase 3)
+  auto flush = [&]() {
+    const bool started_before = nstart < ps || (split && node == 0 && cont_first);
+    const bool continues = nend > pe || (split && node == nn - 1 && cont_last);
+    if (!started_before && !continues) {
+      if (active) M::store(a, a.out + ((int64_t)(n0 + node) * rowstride + eoff) * ESZ, l, acc);
+    } else {
+      const int r = started_before ? 0 : 1;
+      s_pm[r][rec] = m;
+      s_pl[r][rec] = l;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) s_pacc[r][rec * VEC + i] = acc[i];
+      if (started_before) {
+        first_rec = true;
+        rec0_node = node;
+      }
+    }
+  };
+
+  int colsN[U], rowN[U];
+  u32x4 eN[U];
+  float wN[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int p = ps + u;
+    colsN[u] = p < pe ? a.col_idx[p] : 0;
+    rowN[u] = 0;
+    eN[u] = u32x4{0u, 0u, 0u, 0u};
+    wN[u] = 0.f;
+    if constexpr (ROWS)
+      if (p < pe) rowN[u] = edge_row(p);
+    if constexpr (HAS_E)
+      if (p < pe && active) eN[u] = load_e(rowN[u]);
+    if constexpr (AGG)
+      if (p < pe && active) wN[u] = a.w[(int64_t)rowN[u] * a.H + head];
+  }
+  for (int base = ps; base < pe; base += U) {
+    int cols[U], rows[U];
+    u32x4 er[U], kr[U], vr[U];
+    float wt[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      cols[u] = min(max(colsN[u], 0), nmax);
+      rows[u] = rowN[u];
+      er[u] = eN[u];
+      wt[u] = wN[u];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      kr[u] = vr[u] = u32x4{0u, 0u, 0u, 0u};
+      if (base + u < pe && active) {
+        if constexpr (!AGG) kr[u] = ld16(a.k + ((int64_t)cols[u] * rowstride + eoff) * ESZ);
+        vr[u] = ld16(a.v + ((int64_t)cols[u] * rowstride + eoff) * ESZ);
+      }
+    }
+    // prefetch the next piece of indices (and edge rows) while this one computes
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = base + U + u;
+      if (p < pe) {
+        colsN[u] = a.col_idx[p];
+        if constexpr (ROWS) rowN[u] = edge_row(p);
+        if constexpr (HAS_E)
+          if (active) eN[u] = load_e(rowN[u]);
+        if constexpr (AGG)
+          if (active) wN[u] = a.w[(int64_t)rowN[u] * a.H + head];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = base + u;
+      if (p >= pe) break;
+      if (p >= nend) {
+        flush();
+        while (node < nn - 1) {  // next destination with edges (monotone pointers: one step + empties)
+          ++node;
+          nstart = nend;
+          nend = s_rp[node + 1];
+          if (nend > p) break;
+        }
+        m = -INFINITY;
+        l = 0.f;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+        load_q(node);
+      }
+      u32x4 xo;
+      M::step(a, qf, kr[u], er[u], vr[u], wt[u], m, l, acc, xo);
+      if constexpr (EOUT)
+        if (active) st16(a.e_out + ((int64_t)rows[u] * rowstride + eoff) * ESZ, xo);
+    }
+  }
+  if (ps < pe) flush();
+  __syncthreads();
+
+  // ---- phase 2: the slot holding a cut destination's last edge merges its pieces
+  const bool xwg_first = split && cont_first && nn > 0;
+  const bool xwg_last = split && cont_last && nn > 0 && !(nn == 1 && cont_first);
+  if (first_rec && s_rp[rec0_node + 1] <= pe && !(rec0_node == 0 && xwg_first) && !(rec0_node == nn - 1 && xwg_last)) {
+    const int first_slot = min(max((s_rp[rec0_node] - E0) / C, 0), slot);
+    float mm = s_pm[1][first_slot * G + lig], ll = s_pl[1][first_slot * G + lig], aa[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) aa[i] = s_pacc[1][(first_slot * G + lig) * VEC + i];
+    for (int s = first_slot + 1; s <= slot; ++s) {
+      float a2[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) a2[i] = s_pacc[0][(s * G + lig) * VEC + i];
+      M::fold(mm, ll, aa, s_pm[0][s * G + lig], s_pl[0][s * G + lig], a2);
+    }
+    if (active) M::store(a, a.out + ((int64_t)(n0 + rec0_node) * rowstride + eoff) * ESZ, ll, aa);
+  }
+
+  // ---- phase 3: rows cut across workgroups.  Wave 0 takes the first row, wave
+  // 1 the last; its lanes 0..G-1 act as one slot.  The row's records in LDS
+  // are merged in slot order into this workgroup's part, which is written to
+  // the workspace with device-coherent stores; then the part's flag goes up,
+  // and the flags of all parts are read: a part that finds them all raised
+  // merges the parts in order and writes the row.  Of two parts the later to
+  // raise its flag sees the other's (each waits until its stores are done
+  // before reading), so some part merges; parts that merge write identical bits.
+  if (split && lane < G && ((wave == 0 && xwg_first) || (wave == 1 && xwg_last))) {
+    const int kind = wave, nd = kind == 0 ? 0 : nn - 1;
+    const int s0 = min(max((s_rp[nd] - E0) / C, 0), NS - 1);
+    const int t0 = min(max((max(s_rp[nd + 1], s_rp[nd] + 1) - 1 - E0) / C, s0), NS - 1);
+    // the first row's records are all "started before"; the last row starts
+    // inside slot s0's piece
+    const int r0 = kind == 0 ? 0 : 1;
+    float pm = s_pm[r0][s0 * G + lig], pl = s_pl[r0][s0 * G + lig], pa[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) pa[i] = s_pacc[r0][(s0 * G + lig) * VEC + i];
+    for (int sl = s0 + 1; sl <= t0; ++sl) {
+      float a2[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) a2[i] = s_pacc[0][(sl * G + lig) * VEC + i];
+      M::fold(pm, pl, pa, s_pm[0][sl * G + lig], s_pl[0][sl * G + lig], a2);
+    }
+    const int64_t HB_B = (int64_t)gridDim.y * a.num_wg, hb_B = (int64_t)hb * a.num_wg;
+    auto part = [&](int k, int64_t bb) { return (int64_t)k * HB_B + hb_B + bb; };
+    const int64_t row = n0 + nd;
+    {
+      const int64_t me = part(kind, blk) * G + lig;
+      __hip_atomic_store(a.ws_ml + me * 2, pm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.ws_ml + me * 2 + 1, pl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i)
+        __hip_atomic_store(a.ws_acc + me * VEC + i, pa[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);  // the part is at the device coherence point before its flag
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (lig == 0) __hip_atomic_store(a.ws_flags + part(kind, blk), a.token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);  // the flag is up before the other flags are read
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+    {
+      const int64_t rs = min(max(a.row_ptr[row], 0), nnz_i), re = min(max(a.row_ptr[row + 1], 0), nnz_i);
+      const int64_t b0 = (row + rs) / a.items_per_wg, b1 = (row + re - 1) / a.items_per_wg;
+      bool in = true;
+      for (int64_t bb = b0 + lig; bb <= b1; bb += G)
+        in = in && __hip_atomic_load(a.ws_flags + part(bb == b0 ? 1 : 0, bb), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT) == a.token;
+      const uint64_t smask = G == 64 ? ~0ull : ((1ull << G) - 1);
+      if (!(__ballot(!in) & smask)) {
+        auto ld = [&](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+        const int64_t q0 = part(1, b0) * G + lig;
+        float mm = ld(a.ws_ml + q0 * 2), ll = ld(a.ws_ml + q0 * 2 + 1), aa[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) aa[i] = ld(a.ws_acc + q0 * VEC + i);
+        for (int64_t bb = b0 + 1; bb <= b1; ++bb) {
+          const int64_t qb = part(0, bb) * G + lig;
+          float a2[VEC];
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) a2[i] = ld(a.ws_acc + qb * VEC + i);
+          M::fold(mm, ll, aa, ld(a.ws_ml + qb * 2), ld(a.ws_ml + qb * 2 + 1), a2);
+        }
+        if (active) M::store(a, a.out + (row * rowstride + eoff) * ESZ, ll, aa);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch helpers, one set per partition (SPLIT); the two sets are compiled in
+// separate translation units
+// ---------------------------------------------------------------------------
+
+// What a launch computes; the geometry is derived from it.
+struct Problem {
+  int32_t n, H, head_dim;
+  int64_t nnz;
+  gattn_dtype dtype;
+  int mode;
+  bool he, eout;
+};
+
+namespace detail {
+
+template <int MODE, bool HAS_E>
+constexpr int unroll() { return HAS_E ? GATTN_GATHER_U_E : GATTN_GATHER_U; }
+
+template <typename T, int D, int MODE, bool HAS_E, bool EOUT, bool SPLIT>
+constexpr auto kernel_of() { return gather_kernel<T, D, MODE, HAS_E, EOUT, unroll<MODE, HAS_E>(), SPLIT>; }
+
+// Workgroups of one instantiation that fit on a CU at once (queried once).
+template <typename T, int D, int MODE, bool HAS_E, bool EOUT, bool SPLIT>
+int resident_per_cu() {
+  static const int per_cu = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kernel_of<T, D, MODE, HAS_E, EOUT, SPLIT>(), kGatherThreads,
+                                                     0) != hipSuccess)
+      b = 1;
+    return std::max(b, 1);
+  }();
+  return per_cu;
+}
+
+// Calls F::template run<T, D, MODE, HAS_E, EOUT>() for the instantiation of p.
+// The instantiations that exist: standard +-E, clipped +-E (+ edge update
+// with E), aggregate.
+template <typename F, typename T, int D>
+auto by_variant(const Problem& p, const F& f) {
+  if (p.mode == kModeAggregate) return f.template run<T, D, kModeAggregate, false, false>();
+  if (p.mode == GATTN_SOFTMAX_STANDARD)
+    return p.he ? f.template run<T, D, GATTN_SOFTMAX_STANDARD, true, false>()
+                : f.template run<T, D, GATTN_SOFTMAX_STANDARD, false, false>();
+  if (!p.he) return f.template run<T, D, GATTN_SOFTMAX_CLIPPED, false, false>();
+  return p.eout ? f.template run<T, D, GATTN_SOFTMAX_CLIPPED, true, true>()
+                : f.template run<T, D, GATTN_SOFTMAX_CLIPPED, true, false>();
+}
+
+template <typename F, typename T>
+auto by_dim(const Problem& p, const F& f) {
+  switch (p.head_dim) {
+    case 16: return by_variant<F, T, 16>(p, f);
+    case 32: return by_variant<F, T, 32>(p, f);
+    case 64: return by_variant<F, T, 64>(p, f);
+    default: return by_variant<F, T, 128>(p, f);
+  }
+}
+
+template <typename F>
+auto dispatch(const Problem& p, const F& f) {
+  switch (p.dtype) {
+    case GATTN_F32: return by_dim<F, float>(p, f);
+    case GATTN_F16: return by_dim<F, _Float16>(p, f);
+    default: return by_dim<F, bf16_t>(p, f);
+  }
+}
+
+template <bool SPLIT>
+struct Resident {
+  template <typename T, int D, int MODE, bool HAS_E, bool EOUT>
+  int run() const { return resident_per_cu<T, D, MODE, HAS_E, EOUT, SPLIT>(); }
+};
+
+template <bool SPLIT>
+struct Launch {
+  const GatherArgs& ga;
+  dim3 grid;
+  hipStream_t s;
+  template <typename T, int D, int MODE, bool HAS_E, bool EOUT>
+  hipError_t run() const {
+    hipLaunchKernelGGL((kernel_of<T, D, MODE, HAS_E, EOUT, SPLIT>()), grid, dim3(kGatherThreads), 0, s, ga);
+    return hipGetLastError();
+  }
+};
+
+// Defined (explicitly instantiated) in forward_gather.hip for SPLIT = false
+// and in forward_gather_split.hip for SPLIT = true.
+template <bool SPLIT>
+int resident_of(const Problem& p);
+template <bool SPLIT>
+hipError_t launch_kernels(const Problem& p, const GatherArgs& ga, dim3 grid, hipStream_t s);
+
+template <>
+int resident_of<false>(const Problem& p);
+template <>
+int resident_of<true>(const Problem& p);
+template <>
+hipError_t launch_kernels<false>(const Problem& p, const GatherArgs& ga, dim3 grid, hipStream_t s);
+template <>
+hipError_t launch_kernels<true>(const Problem& p, const GatherArgs& ga, dim3 grid, hipStream_t s);
+
+template <bool SPLIT>
+int resident_impl(const Problem& p) { return dispatch(p, Resident<SPLIT>{}); }
+template <bool SPLIT>
+hipError_t launch_impl(const Problem& p, const GatherArgs& ga, dim3 grid, hipStream_t s) {
+  return dispatch(p, Launch<SPLIT>{ga, grid, s});
+}
+
+}  // namespace detail
+}  // namespace gattn

@@ -42,6 +42,9 @@ hipError_t launch_rowwindows_fill(int32_t n, int64_t nnz, const int32_t* row_ptr
 hipError_t launch_forward_gather(const gattn_forward_args& a, hipStream_t s);
 hipError_t launch_forward_mfma(const gattn_forward_args& a, hipStream_t s);
 hipError_t launch_aggregate_gather(const gattn_aggregate_args& a, hipStream_t s);
+// bytes of the workspace that selects the balanced partition (0 for N = 0)
+size_t forward_gather_workspace_bytes(const gattn_forward_args& a);
+size_t aggregate_workspace_bytes(const gattn_aggregate_args& a);
 // applicability of the MFMA row-window path (no launch)
 bool mfma_supported(const gattn_forward_args& a);
 

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GATTN_ABI_VERSION 2
+#define GATTN_ABI_VERSION 3
 
 #ifndef GATTN_API
 #define GATTN_API __attribute__((visibility("default")))
@@ -190,6 +190,17 @@ typedef struct {
      clamp(scale * q[dst] * k[src], clip_lo, clip_hi) * e[r], the product before
      the feature sum.  Must not alias any input or out.                         */
   void* e_out;
+  /* Optional workspace (gather path): when given, workgroups take equal shares
+     of the edges (a merge path over row ends and edges) and a destination with
+     more in-edges than about half a share is cut into edge-parallel parts
+     whose partial softmax states are merged in order (Fused3S Figure 2's
+     node- versus edge-parallel split).  Without it, workgroups take equal
+     numbers of destinations.  Size from gattn_forward_workspace; 256-byte
+     aligned; any contents on entry (flags are tagged per call); must not
+     alias any other argument; one workspace must not serve two calls that
+     run at the same time.  Ignored on the MFMA path.                           */
+  void* workspace;
+  size_t workspace_bytes;
 } gattn_forward_args;
 
 /* out[i, h, :] = sum_p alpha_p(h) v[col_idx[p], h, :] over the in-edges p of i;
@@ -201,6 +212,11 @@ GATTN_API gattn_status gattn_forward(const gattn_forward_args* args /*[host]*/, 
 
 /* The path gattn_forward would take for these arguments (no work enqueued; `out` may be NULL). */
 GATTN_API gattn_status gattn_forward_path(const gattn_forward_args* args /*[host]*/, gattn_path* path /*[host]*/);
+
+/* Workspace bytes for the balanced gather partition of these arguments (sizes,
+ * dtype, mode, whether e and e_out are given; pointers are not read).  0 when
+ * there is nothing to compute.  Depends on the current device's CU count. */
+GATTN_API gattn_status gattn_forward_workspace(const gattn_forward_args* args /*[host]*/, size_t* bytes /*[host]*/);
 
 /* ------------------------------------------------------------------------
  * gattn_aggregate: weighted aggregation over the CSR with given per-edge
@@ -230,9 +246,15 @@ typedef struct {
   int32_t normalize;           /* 0: weighted sum; 1: divided by (sum of w + eps)    */
   float eps;                   /* >= 0                                               */
   uint32_t flags;              /* GATTN_FLAG_VALIDATE                                */
+  void* workspace;             /* optional; as in gattn_forward_args                 */
+  size_t workspace_bytes;
 } gattn_aggregate_args;
 
 GATTN_API gattn_status gattn_aggregate(const gattn_aggregate_args* args /*[host]*/, hipStream_t stream);
+
+/* Workspace bytes for the balanced partition of gattn_aggregate (sizes, dtype;
+ * `out` may be NULL and no pointer is read). */
+GATTN_API gattn_status gattn_aggregate_workspace(const gattn_aggregate_args* args /*[host]*/, size_t* bytes /*[host]*/);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(gsa):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     lib = ctypes.CDLL(gsa.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), f"{name} declared in gattn.h but not exported"
@@ -46,11 +46,11 @@ def test_enums_and_strings(gsa):
                  "GATTN_ERR_DUPLICATE_EDGE", "GATTN_ERR_BUFFER_TOO_SMALL", "GATTN_ERR_HIP"]:
         m = re.search(name + r"\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(gsa, name)
-    assert gsa.gattn_abi_version() == 2
+    assert gsa.gattn_abi_version() == 3
     assert gsa.gattn_status_string(gsa.GATTN_ERR_DUPLICATE_EDGE).startswith("repeated")
     assert gsa.gattn_status_string(99) == "unknown status"
-    assert ctypes.sizeof(gsa._ForwardArgs) == 144
-    assert ctypes.sizeof(gsa._AggregateArgs) == 88
+    assert ctypes.sizeof(gsa._ForwardArgs) == 160
+    assert ctypes.sizeof(gsa._AggregateArgs) == 104
 
 
 def fake_args(gsa, **kw):
@@ -106,6 +106,8 @@ def test_forward_argument_errors(gsa):
         (dict(e_out=(1 << 32) + (16 << 20) + 8, e=(1 << 32) + (14 << 20), mode=gsa.GATTN_SOFTMAX_CLIPPED),
          gsa.GATTN_ERR_INVALID_VALUE),                                 # misaligned
         (dict(edge_ids=(1 << 32) + 2), gsa.GATTN_ERR_INVALID_VALUE),   # misaligned
+        (dict(workspace=(1 << 32) + (20 << 20) + 64, workspace_bytes=4096), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(workspace=(1 << 32) + (8 << 20), workspace_bytes=4096), gsa.GATTN_ERR_INVALID_VALUE),  # aliases out
     ]
     for kw, want in cases:
         a = fake_args(gsa, **kw)
@@ -189,6 +191,8 @@ def test_aggregate_argument_errors(gsa):
         (dict(w=base + (4 << 20) + 2), gsa.GATTN_ERR_INVALID_VALUE),
         (dict(out=base + (2 << 20) + 4096), gsa.GATTN_ERR_INVALID_VALUE),  # aliases x
         (dict(out=base + (4 << 20)), gsa.GATTN_ERR_INVALID_VALUE),         # aliases w
+        (dict(workspace=base + (8 << 20) + 128, workspace_bytes=4096), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(workspace=base + (2 << 20), workspace_bytes=4096), gsa.GATTN_ERR_INVALID_VALUE),  # aliases x
     ]
     for kw, want in cases:
         a = fake_aggregate(gsa, **kw)
@@ -197,3 +201,19 @@ def test_aggregate_argument_errors(gsa):
     # nothing to do: no launch, no HIP call
     a = fake_aggregate(gsa, num_nodes=0, nnz=0, row_ptr=None, x=None, w=None, out=None)
     assert L.gattn_aggregate(ctypes.byref(a), None) == gsa.GATTN_OK
+
+
+def test_workspace_query_errors(gsa):
+    L = gsa._lib
+    nb = ctypes.c_size_t(7)
+    a = fake_args(gsa)
+    assert L.gattn_forward_workspace(ctypes.byref(a), None) == gsa.GATTN_ERR_INVALID_VALUE
+    assert L.gattn_forward_workspace(None, ctypes.byref(nb)) == gsa.GATTN_ERR_INVALID_VALUE
+    a = fake_args(gsa, head_dim=24)
+    assert L.gattn_forward_workspace(ctypes.byref(a), ctypes.byref(nb)) == gsa.GATTN_ERR_UNSUPPORTED
+    g = fake_aggregate(gsa, normalize=3)
+    assert L.gattn_aggregate_workspace(ctypes.byref(g), ctypes.byref(nb)) == gsa.GATTN_ERR_INVALID_VALUE
+    assert nb.value == 7   # untouched on error
+    # nothing to compute: no workspace, no HIP call
+    a = fake_args(gsa, num_nodes=0, nnz=0)
+    assert L.gattn_forward_workspace(ctypes.byref(a), ctypes.byref(nb)) == gsa.GATTN_OK and nb.value == 0

@@ -18,21 +18,22 @@ def gsa():
     return g
 
 
-def gpu_forward(gsa, c, path="gather", rw=None, rp=None, ci=None):
+def gpu_forward(gsa, c, path="gather", rw=None, rp=None, ci=None, workspace=True):
     wl = c.wl
     rp_t = torch.from_numpy(c.rp if rp is None else rp).cuda()
     ci_t = torch.from_numpy(c.ci if ci is None else ci).cuda()
     return gsa.gattn_forward(rp_t, ci_t, c.q, c.k, c.v, c.e, mode=wl.mode, scale=wl.scale, clip=wl.clip,
-                             eps=wl.eps, path=path, rw=rw)
+                             eps=wl.eps, path=path, rw=rw, workspace=workspace)
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 5])
-def test_configs_gather(gsa, cfg):
+@pytest.mark.parametrize("partition", ["balanced", "node"])
+def test_configs_gather(gsa, cfg, partition):
     c = case(cfg)
     ref, mag = c.oracle_forward()
-    out = gpu_forward(gsa, c, "gather")
+    out = gpu_forward(gsa, c, "gather", workspace=partition == "balanced")
     err = check_forward(out, ref, mag, c.wl.dtype)
-    print(f"config {cfg} gather: error {err:.3e}")
+    print(f"config {cfg} gather ({partition} partition): error {err:.3e}")
 
 
 def test_config5_mfma(gsa):
@@ -103,7 +104,7 @@ def test_matrix_mfma(gsa, dtype, hd, n):
     check_forward(out, ref, mag, dtype)
 
 
-@pytest.mark.parametrize("path", ["gather", "mfma"])
+@pytest.mark.parametrize("path", ["gather", "gather-node", "mfma"])
 def test_hubs_and_isolated(gsa, path):
     # destinations far above a workgroup's share (split over all slots and
     # merged in LDS), isolated destinations, single in-edges
@@ -126,7 +127,8 @@ def test_hubs_and_isolated(gsa, path):
     ref, mag = oracle.forward(rp, ci, oracle.widen(q), oracle.widen(k), oracle.widen(v), scale=scale, want_mag=True)
     rp_t, ci_t = torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda()
     rw = gsa.gattn_build_rowwindows(rp_t, ci_t, n) if path == "mfma" else None
-    out = gsa.gattn_forward(rp_t, ci_t, q.cuda(), k.cuda(), v.cuda(), scale=scale, path=path, rw=rw)
+    out = gsa.gattn_forward(rp_t, ci_t, q.cuda(), k.cuda(), v.cuda(), scale=scale, path=path.split("-")[0], rw=rw,
+                            workspace=path != "gather-node")
     check_forward(out, ref, mag, dtype)
     deg = np.diff(rp)
     one = np.flatnonzero(deg == 1)
@@ -144,11 +146,13 @@ def test_empty_and_edge_cases(gsa):
         assert out.shape == q.shape and torch.all(out == 0)
 
 
-def test_deterministic(gsa):
-    c = case(2)
-    a = gpu_forward(gsa, c)
-    b = gpu_forward(gsa, c)
-    assert torch.equal(a, b)
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_deterministic(gsa, cfg):
+    c = case(cfg)
+    for workspace in (True, None):
+        a = gpu_forward(gsa, c, workspace=workspace)
+        b = gpu_forward(gsa, c, workspace=workspace)
+        assert torch.equal(a, b)
 
 
 def test_argument_errors(gsa):
