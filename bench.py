@@ -69,7 +69,7 @@ def parse():
     p.add_argument("--config", type=int, default=2)
     p.add_argument("--path", default="auto", choices=["auto", "gather", "mfma"])
     p.add_argument("--variant", default="forward", choices=list(VARIANTS))
-    p.add_argument("--partition", default="balanced", choices=["balanced", "node"],
+    p.add_argument("--partition", default="node", choices=["balanced", "node"],
                    help="gather path: edge-balanced workgroups with cut heavy rows (workspace) or equal node counts")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bound of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true")

@@ -312,13 +312,15 @@ def gattn_forward(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch.Tensor,
                   e: Optional[torch.Tensor] = None, mode: str = "standard", scale: Optional[float] = None,
                   clip=(-5.0, 5.0), eps: float = 1e-6, path: str = "auto", rw: Optional[RowWindows] = None,
                   out: Optional[torch.Tensor] = None, validate: bool = False,
-                  edge_ids: Optional[torch.Tensor] = None, e_out=None, workspace=True):
+                  edge_ids: Optional[torch.Tensor] = None, e_out=None, workspace=None):
     """Fused SDDMM -> softmax -> SpMM over the CSR; q/k/v [N, H, D]; e
     [nnz, H, D] by CSR position (or row edge_ids[p] for position p) or None.
     Returns out [N, H, D]; with e_out (True, or an [nnz, H, D] tensor) the
     clipped mode also writes the per-edge update and returns (out, e_out).
-    workspace: True (default) allocates the balanced-partition workspace, a
-    uint8 tensor supplies it, None runs the node partition."""
+    workspace: None (default) runs the node partition (equal destination
+    counts per workgroup); True allocates the balanced-partition workspace
+    and a uint8 tensor supplies it (equal edge shares, heavy rows cut across
+    workgroups: for graphs whose hubs hold many times a workgroup's share)."""
     row_ptr, col_idx = _i32(row_ptr, "row_ptr"), _i32(col_idx, "col_idx")
     if q.dim() != 3 or not q.is_contiguous() or not q.is_cuda:
         raise ValueError("q must be a contiguous [N, H, D] GPU tensor")
@@ -360,7 +362,7 @@ def gattn_forward_path(row_ptr, col_idx, q, k, v, e=None, mode="standard", path=
 
 def gattn_aggregate(row_ptr: torch.Tensor, col_idx: torch.Tensor, x: torch.Tensor, w: torch.Tensor,
                     normalize: bool = False, eps: float = 1e-6, edge_ids: Optional[torch.Tensor] = None,
-                    out: Optional[torch.Tensor] = None, validate: bool = False, workspace=True) -> torch.Tensor:
+                    out: Optional[torch.Tensor] = None, validate: bool = False, workspace=None) -> torch.Tensor:
     """Weighted aggregation over the CSR: x [N, H, D], w [nnz, H] fp32 (row
     edge_ids[p] for position p when given); out[i] = sum_p w x[src], divided
     by (sum_p w + eps) when normalize.  workspace as in gattn_forward."""

@@ -10,10 +10,10 @@
 namespace gattn {
 namespace detail {
 template <>
-int resident_of<false>(const Problem& p) { return resident_impl<false>(p); }
+int resident_of<kPartNode>(const Problem& p) { return resident_impl<kPartNode>(p); }
 template <>
-hipError_t launch_kernels<false>(const Problem& p, const GatherArgs& ga, dim3 grid, hipStream_t s) {
-  return launch_impl<false>(p, ga, grid, s);
+hipError_t launch_kernels<kPartNode>(const Problem& p, const GatherArgs& ga, dim3 grid, hipStream_t s) {
+  return launch_impl<kPartNode>(p, ga, grid, s);
 }
 }  // namespace detail
 
@@ -31,8 +31,30 @@ int device_cus() {
   return cus[dev];
 }
 
+// Heads per workgroup and slot width: a slot of G lanes (16 bytes each) holds
+// one edge's slice of HB heads.
+struct Geom {
+  int hb, log2g, G, vec, head_blocks, ns, qrow;
+};
+
+Geom make_geom(const Problem& p, int hb_max) {
+  Geom g{};
+  const int esz = p.dtype == GATTN_F32 ? 4 : 2;
+  g.vec = 16 / esz;
+  const int lph = p.head_dim / g.vec;
+  g.hb = std::max(1, std::min({p.H, 64 / lph, hb_max}));
+  g.G = 1;
+  while (g.G < g.hb * lph) g.G <<= 1;
+  g.log2g = 0;
+  while ((1 << g.log2g) < g.G) ++g.log2g;
+  g.head_blocks = (int)ceil_div(p.H, g.hb);
+  g.ns = 4 * (64 / g.G);
+  g.qrow = g.hb * p.head_dim * esz;
+  return g;
+}
+
 struct Plan {
-  int hb, log2g, G, vec, head_blocks;
+  Geom geo;                 // node and balanced partitions
   int npw;                  // node partition: destinations per workgroup
   int64_t C, B;             // balanced partition: items per workgroup, workgroups per head block
   int light_max;
@@ -41,61 +63,59 @@ struct Plan {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Heads per workgroup, slot width, and the partition.  Both partitions aim at
-// about EDGES_PER_SLOT * U edges per slot and round the grid to whole "rounds"
-// of co-resident workgroups (a last, partly filled round would leave most CUs
-// idle while it runs).  The node partition is bounded by the LDS that stages
-// Q rows; the balanced one keeps its typical row count under that bound.
+// Destinations per workgroup for an equal-count partition: about `target`
+// edges each, at most `cap`, and the grid rounded to whole "rounds" of
+// co-resident workgroups (a last, partly filled round would leave most CUs
+// idle while it runs).
+int nodes_per_wg(const Problem& p, double target, int cap, int head_blocks, int64_t resident_all) {
+  const int64_t per_round = std::max<int64_t>(1, resident_all / head_blocks);
+  const double avg = (double)p.nnz / p.n;
+  int npw_target = cap;
+  if (avg > 0) npw_target = (int)std::min<double>(cap, std::max(1.0, std::ceil(target / avg)));
+  const double wgs = (double)ceil_div(p.n, npw_target) * head_blocks;
+  const int64_t rounds = std::max<int64_t>(1, (int64_t)std::llround(wgs / (double)resident_all));
+  return (int)std::min<int64_t>(cap, std::max<int64_t>(1, ceil_div(p.n, rounds * per_round)));
+}
+
+// Both partitions aim at about EDGES_PER_SLOT * U edges per slot.  The node
+// partition is bounded by the LDS that stages Q rows; the balanced one keeps
+// its typical row count under that bound.
 Plan make_plan(const Problem& p) {
   Plan g{};
-  const int esz = p.dtype == GATTN_F32 ? 4 : 2;
-  g.vec = 16 / esz;
-  const int lph = p.head_dim / g.vec;
-  g.hb = std::min(p.H, 64 / lph);
-  g.G = 1;
-  while (g.G < g.hb * lph) g.G <<= 1;
-  g.log2g = 0;
-  while ((1 << g.log2g) < g.G) ++g.log2g;
-  g.head_blocks = (int)ceil_div(p.H, g.hb);
-  const int ns = 4 * (64 / g.G);
-  const int u = p.he ? GATTN_GATHER_U_E : GATTN_GATHER_U;
-  const double target = (double)ns * GATTN_GATHER_EDGES_PER_SLOT * u;   // edges per workgroup
-  const int qrow = g.hb * p.head_dim * esz;
-  const int qcap = p.mode == kModeAggregate ? kMaxNodesPerWg : std::max(1, std::min(kMaxNodesPerWg, kQLdsBytes / qrow));
+  g.geo = make_geom(p, 64);
   if (p.n == 0) return g;
-  const int64_t resident_all = (int64_t)detail::resident_of<false>(p) * device_cus();
-  const int64_t per_round = std::max<int64_t>(1, resident_all / g.head_blocks);
-  const int64_t resident_split = (int64_t)detail::resident_of<true>(p) * device_cus();
-  const int64_t per_round_split = std::max<int64_t>(1, resident_split / g.head_blocks);
+  const int u = p.he ? GATTN_GATHER_U_E : GATTN_GATHER_U;
+  const int cus = device_cus();
+  auto qcap_of = [&](const Geom& ge) {
+    return p.mode == kModeAggregate ? kMaxNodesPerWg : std::max(1, std::min(kMaxNodesPerWg, kQLdsBytes / ge.qrow));
+  };
 
   // node partition
-  const double avg = (double)p.nnz / p.n;
-  int npw_target = qcap;
-  if (avg > 0) npw_target = (int)std::min<double>(qcap, std::max(1.0, std::ceil(target / avg)));
-  {
-    const double wgs = (double)ceil_div(p.n, npw_target) * g.head_blocks;
-    const int64_t rounds = std::max<int64_t>(1, (int64_t)std::llround(wgs / (double)resident_all));
-    g.npw = (int)std::min<int64_t>(qcap, std::max<int64_t>(1, ceil_div(p.n, rounds * per_round)));
-  }
+  const int qcap = qcap_of(g.geo);
+  const double target = (double)g.geo.ns * GATTN_GATHER_EDGES_PER_SLOT * u;  // edges per workgroup
+  g.npw = nodes_per_wg(p, target, qcap, g.geo.head_blocks, (int64_t)detail::resident_of<kPartNode>(p) * cus);
 
   // balanced partition over T = N + nnz items
-  const int64_t T = (int64_t)p.n + p.nnz;
-  const int64_t cmax = kMaxNodesPerWg - 2;
-  double c0 = p.nnz > 0 ? target * (double)T / (double)p.nnz : (double)cmax;
-  c0 = std::min(c0, (double)qcap * (double)T / (double)p.n);   // typical rows per workgroup <= qcap
-  int64_t C = std::min<int64_t>(cmax, std::max<int64_t>(8, (int64_t)c0));
   {
-    const double wgs = (double)ceil_div(T, C) * g.head_blocks;
+    const int64_t resident_split = (int64_t)detail::resident_of<kPartSplit>(p) * cus;
+    const int64_t per_round_split = std::max<int64_t>(1, resident_split / g.geo.head_blocks);
+    const int64_t T = (int64_t)p.n + p.nnz;
+    const int64_t cmax = kMaxNodesPerWg - 2;
+    double c0 = p.nnz > 0 ? target * (double)T / (double)p.nnz : (double)cmax;
+    c0 = std::min(c0, (double)qcap * (double)T / (double)p.n);   // typical rows per workgroup <= qcap
+    int64_t C = std::min<int64_t>(cmax, std::max<int64_t>(8, (int64_t)c0));
+    const double wgs = (double)ceil_div(T, C) * g.geo.head_blocks;
     const int64_t rounds = std::max<int64_t>(1, (int64_t)std::llround(wgs / (double)resident_split));
     C = std::min<int64_t>(cmax, std::max<int64_t>(8, ceil_div(T, rounds * per_round_split)));
+    g.C = C;
+    g.B = ceil_div(T, C);
+    g.light_max = (int)std::max<int64_t>(2, C / 2);
+    const size_t parts = (size_t)2 * g.geo.head_blocks * g.B;
+    g.off_ml = align256(parts * sizeof(uint64_t));
+    g.off_acc = g.off_ml + align256(parts * g.geo.G * 2 * sizeof(float));
+    g.ws_bytes = g.off_acc + align256(parts * g.geo.G * g.geo.vec * sizeof(float));
   }
-  g.C = C;
-  g.B = ceil_div(T, C);
-  g.light_max = (int)std::max<int64_t>(2, C / 2);
-  const size_t parts = (size_t)2 * g.head_blocks * g.B;
-  g.off_ml = align256(parts * sizeof(uint64_t));
-  g.off_acc = g.off_ml + align256(parts * g.G * 2 * sizeof(float));
-  g.ws_bytes = g.off_acc + align256(parts * g.G * g.vec * sizeof(float));
+
   return g;
 }
 
@@ -114,16 +134,14 @@ uint64_t next_token() {
 }
 
 // ga carries the pointers and scalars; the geometry fields are filled here.
-// A workspace (of at least the plan's size) selects the balanced partition.
-hipError_t launch_gather(GatherArgs ga, const Problem& p, void* ws, hipStream_t s) {
+hipError_t launch_gather(GatherArgs ga, const Problem& p, int part, void* ws, hipStream_t s) {
   if (p.n == 0) return hipSuccess;
   const Plan g = make_plan(p);
-  ga.HB = g.hb;
-  ga.log2G = g.log2g;
-  ga.npw = g.npw;
+  const Geom& ge = g.geo;
+  ga.HB = ge.hb;
+  ga.log2G = ge.log2g;
   ga.ws_flags = nullptr;
-  dim3 grid((unsigned)ceil_div(p.n, g.npw), (unsigned)g.head_blocks);
-  if (ws) {
+  if (part == kPartSplit) {
     uint8_t* w = (uint8_t*)ws;
     ga.ws_flags = (uint64_t*)w;
     ga.ws_ml = (float*)(w + g.off_ml);
@@ -133,9 +151,10 @@ hipError_t launch_gather(GatherArgs ga, const Problem& p, void* ws, hipStream_t 
     ga.light_max = g.light_max;
     ga.num_wg = (int32_t)g.B;
     ga.token = next_token();
-    grid.x = (unsigned)g.B;
+    return detail::launch_kernels<kPartSplit>(p, ga, dim3((unsigned)g.B, (unsigned)ge.head_blocks), s);
   }
-  return ws ? detail::launch_kernels<true>(p, ga, grid, s) : detail::launch_kernels<false>(p, ga, grid, s);
+  ga.npw = g.npw;
+  return detail::launch_kernels<kPartNode>(p, ga, dim3((unsigned)ceil_div(p.n, ga.npw), (unsigned)ge.head_blocks), s);
 }
 
 Problem forward_problem(const gattn_forward_args& a) {
@@ -147,6 +166,9 @@ Problem forward_problem(const gattn_forward_args& a) {
 Problem aggregate_problem(const gattn_aggregate_args& a) {
   return Problem{a.num_nodes, a.num_heads, a.head_dim, a.nnz, a.dtype, kModeAggregate, false, false};
 }
+
+// A workspace selects the balanced partition.
+int pick_part(const void* ws) { return ws ? kPartSplit : kPartNode; }
 
 }  // namespace
 
@@ -176,7 +198,7 @@ hipError_t launch_forward_gather(const gattn_forward_args& a, hipStream_t s) {
   ga.eps = a.eps;
   ga.ids = a.e ? a.edge_ids : nullptr;
   ga.e_out = (uint8_t*)a.e_out;
-  return launch_gather(ga, forward_problem(a), a.workspace, s);
+  return launch_gather(ga, forward_problem(a), pick_part(a.workspace), a.workspace, s);
 }
 
 hipError_t launch_aggregate_gather(const gattn_aggregate_args& a, hipStream_t s) {
@@ -192,7 +214,7 @@ hipError_t launch_aggregate_gather(const gattn_aggregate_args& a, hipStream_t s)
   ga.ids = a.edge_ids;
   ga.w = a.w;
   ga.normalize = a.normalize;
-  return launch_gather(ga, aggregate_problem(a), a.workspace, s);
+  return launch_gather(ga, aggregate_problem(a), pick_part(a.workspace), a.workspace, s);
 }
 
 }  // namespace gattn

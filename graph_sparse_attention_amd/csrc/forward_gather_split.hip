@@ -7,10 +7,10 @@
 namespace gattn {
 namespace detail {
 template <>
-int resident_of<true>(const Problem& p) { return resident_impl<true>(p); }
+int resident_of<kPartSplit>(const Problem& p) { return resident_impl<kPartSplit>(p); }
 template <>
-hipError_t launch_kernels<true>(const Problem& p, const GatherArgs& ga, dim3 grid, hipStream_t s) {
-  return launch_impl<true>(p, ga, grid, s);
+hipError_t launch_kernels<kPartSplit>(const Problem& p, const GatherArgs& ga, dim3 grid, hipStream_t s) {
+  return launch_impl<kPartSplit>(p, ga, grid, s);
 }
 }  // namespace detail
 }  // namespace gattn

@@ -46,6 +46,7 @@
 #pragma once
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -65,6 +66,9 @@
 #ifndef GATTN_GATHER_E_STREAMING
 #define GATTN_GATHER_E_STREAMING 1      // non-temporal loads for the edge tensor
 #endif
+#ifndef GATTN_GATHER_MIN_WAVES
+#define GATTN_GATHER_MIN_WAVES 1        // waves per SIMD the register budget must allow
+#endif
 #ifndef GATTN_XCD_REMAP
 #define GATTN_XCD_REMAP 1
 #endif
@@ -75,6 +79,10 @@ constexpr int kGatherThreads = 256;
 constexpr int kMaxNodesPerWg = 1024;
 constexpr int kQLdsBytes = GATTN_GATHER_Q_LDS_BYTES;
 constexpr int kModeAggregate = 2;  // given per-edge weights instead of logits and softmax
+
+// How workgroups divide the CSR (the kernel's PART parameter).
+constexpr int kPartNode = 0;    // equal numbers of destinations
+constexpr int kPartSplit = 1;   // equal ranges of row ends + edges; heavy rows cut across workgroups
 
 struct GatherArgs {
   const int32_t* __restrict__ row_ptr;
@@ -225,8 +233,8 @@ struct EdgeMath {
   }
 };
 
-template <typename T, int D, int MODE, bool HAS_E, bool EOUT, int U, bool SPLIT>
-__global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
+template <typename T, int D, int MODE, bool HAS_E, bool EOUT, int U, int PART>
+__global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather_kernel(GatherArgs a) {
   using M = EdgeMath<T, D, MODE, HAS_E, EOUT>;
   constexpr int VEC = Elem<T>::kVec;
   constexpr int LPH = D / VEC;
@@ -263,7 +271,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
 
   const int blk = GATTN_XCD_REMAP ? (int)xcd_contiguous_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
   const int nnz_i = (int)a.nnz;
-  constexpr bool split = SPLIT;  // balanced partition (ranges of row ends + edges, cut heavy rows)
+  constexpr bool split = PART == kPartSplit;  // ranges of row ends + edges, cut heavy rows
   int n0, nn;
   bool cont_first = false, cont_last = false;
   if constexpr (split) {
@@ -304,6 +312,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
     }
   }
   __syncthreads();
+
   for (int t = tid; t < nn * chunks; t += kGatherThreads) {
     const int li = t / chunks, c = t - li * chunks;
     if (s_rp[li + 1] - s_rp[li] <= 0)
@@ -340,20 +349,34 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
   float qf[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) qf[i] = 0.f;
+  // Q of local destination nd: from LDS when staged there; the value is
+  // widened inside each branch so that no wait for the global load is left
+  // pending where the branches join
   auto load_q = [&](int nd) {
     if constexpr (!AGG) {
       if (!active) return;
-      const u32x4 qv = nd < qcap ? *reinterpret_cast<const u32x4*>(s_q + nd * qrow + lig * 16)
-                                 : ld16(a.q + ((int64_t)(n0 + nd) * rowstride + eoff) * ESZ);
-      Conv<T>::widen(qv, qf);
+      if (nd < qcap) {
+        Conv<T>::widen(*reinterpret_cast<const u32x4*>(s_q + nd * qrow + lig * 16), qf);
+      } else {
+        Conv<T>::widen(ld16(a.q + ((int64_t)(n0 + nd) * rowstride + eoff) * ESZ), qf);
+      }
     }
   };
   if (ps < pe) load_q(node);
 
+  // Addresses: a row of K / V / E / the edge update is rowbytes long (< 4 MB),
+  // and this lane's 16 bytes sit at lane_b inside it (0 for idle lanes, whose
+  // loads are issued like the others and never used).
+  const uint32_t rowbytes = (uint32_t)(rowstride * ESZ);
+  const uint64_t lane_b = active ? (uint64_t)eoff * ESZ : 0;
+  const int hw = active ? head : 0;
+  auto row_ptr16 = [&](const uint8_t* base, int row) -> const uint8_t* {
+    return base + lane_b + (uint64_t)(uint32_t)row * rowbytes;
+  };
   // row of the per-edge tensors for CSR position p (clamped like the sources)
   auto edge_row = [&](int p) -> int { return a.ids ? min(max(a.ids[p], 0), nnz_i - 1) : p; };
   auto load_e = [&](int row) -> u32x4 {
-    const uint8_t* ptr = a.e + ((int64_t)row * rowstride + eoff) * ESZ;
+    const uint8_t* ptr = row_ptr16(a.e, row);
     return GATTN_GATHER_E_STREAMING ? ld16_stream(ptr) : ld16(ptr);
   };
 
@@ -376,77 +399,105 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
     }
   };
 
-  int colsN[U], rowN[U];
-  u32x4 eN[U];
-  float wN[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int p = ps + u;
-    colsN[u] = p < pe ? a.col_idx[p] : 0;
-    rowN[u] = 0;
-    eN[u] = u32x4{0u, 0u, 0u, 0u};
-    wN[u] = 0.f;
-    if constexpr (ROWS)
-      if (p < pe) rowN[u] = edge_row(p);
-    if constexpr (HAS_E)
-      if (p < pe && active) eN[u] = load_e(rowN[u]);
-    if constexpr (AGG)
-      if (p < pe && active) wN[u] = a.w[(int64_t)rowN[u] * a.H + head];
-  }
-  for (int base = ps; base < pe; base += U) {
-    int cols[U], rows[U];
-    u32x4 er[U], kr[U], vr[U];
-    float wt[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      cols[u] = min(max(colsN[u], 0), nmax);
-      rows[u] = rowN[u];
-      er[u] = eN[u];
-      wt[u] = wN[u];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      kr[u] = vr[u] = u32x4{0u, 0u, 0u, 0u};
-      if (base + u < pe && active) {
-        if constexpr (!AGG) kr[u] = ld16(a.k + ((int64_t)cols[u] * rowstride + eoff) * ESZ);
-        vr[u] = ld16(a.v + ((int64_t)cols[u] * rowstride + eoff) * ESZ);
+  // The edge loop.  Every load is issued without a branch around it: a
+  // position past the slot's piece is clamped to its last edge (or to
+  // position 0 for a slot without edges) and its rows are never used.  So the
+  // compiler's in-order wait counts stay exact and a step waits for its own
+  // K / V rows only, not for the column indices and edge rows of the next
+  // step, which are in flight while it computes (edge ids, which the edge
+  // rows depend on, run two steps ahead).  Divergent lanes run both sides of
+  // a branch, so a global load on either side would make every later use
+  // wait for all loads in flight: the choice below is workgroup-uniform.
+  //  Q_LDS: every destination's Q row is staged in LDS.
+  const int plast = max(pe - 1, 0);
+  auto raw_row = [&](int p) -> int { return a.ids ? a.ids[p] : p; };
+  auto fix_row = [&](int r) -> int { return a.ids ? min(max(r, 0), nnz_i - 1) : r; };
+  auto edge_loop = [&](auto q_lds) {
+    constexpr bool Q_LDS = decltype(q_lds)::value;
+    auto get_q = [&](int nd) {
+      if constexpr (Q_LDS && !AGG) {
+        if (active) Conv<T>::widen(*reinterpret_cast<const u32x4*>(s_q + nd * qrow + lig * 16), qf);
+      } else {
+        load_q(nd);
       }
-    }
-    // prefetch the next piece of indices (and edge rows) while this one computes
+    };
+    int cN[U], rN[U], rNN[U];
+    u32x4 eN[U];
+    float wN[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int p = base + U + u;
-      if (p < pe) {
-        colsN[u] = a.col_idx[p];
-        if constexpr (ROWS) rowN[u] = edge_row(p);
-        if constexpr (HAS_E)
-          if (active) eN[u] = load_e(rowN[u]);
-        if constexpr (AGG)
-          if (active) wN[u] = a.w[(int64_t)rowN[u] * a.H + head];
+      const int p = min(ps + u, plast);
+      cN[u] = a.col_idx[p];
+      rN[u] = 0;
+      rNN[u] = 0;
+      eN[u] = u32x4{0u, 0u, 0u, 0u};
+      wN[u] = 0.f;
+      if constexpr (ROWS) {
+        rN[u] = fix_row(raw_row(p));
+        rNN[u] = raw_row(min(ps + U + u, plast));
       }
+      if constexpr (HAS_E) eN[u] = load_e(rN[u]);
+      if constexpr (AGG) wN[u] = a.w[(int64_t)rN[u] * a.H + hw];
     }
+    for (int base = ps; base < pe; base += U) {
+      int cols[U], rows[U];
+      u32x4 er[U], kr[U], vr[U];
+      float wt[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int p = base + u;
-      if (p >= pe) break;
-      if (p >= nend) {
-        flush();
-        while (node < nn - 1) {  // next destination with edges (monotone pointers: one step + empties)
-          ++node;
-          nstart = nend;
-          nend = s_rp[node + 1];
-          if (nend > p) break;
+      for (int u = 0; u < U; ++u) {
+        cols[u] = min(max(cN[u], 0), nmax);
+        rows[u] = rN[u];
+        er[u] = eN[u];
+        wt[u] = wN[u];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        kr[u] = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (!AGG) kr[u] = ld16(row_ptr16(a.k, cols[u]));
+        vr[u] = ld16(row_ptr16(a.v, cols[u]));
+      }
+      // the next step's indices and edge rows, in flight while this one computes
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        cN[u] = a.col_idx[min(base + U + u, plast)];
+        if constexpr (ROWS) {
+          rN[u] = fix_row(rNN[u]);
+          rNN[u] = raw_row(min(base + 2 * U + u, plast));
         }
-        m = -INFINITY;
-        l = 0.f;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-        load_q(node);
+        if constexpr (HAS_E) eN[u] = load_e(rN[u]);
+        if constexpr (AGG) wN[u] = a.w[(int64_t)rN[u] * a.H + hw];
       }
-      u32x4 xo;
-      M::step(a, qf, kr[u], er[u], vr[u], wt[u], m, l, acc, xo);
-      if constexpr (EOUT)
-        if (active) st16(a.e_out + ((int64_t)rows[u] * rowstride + eoff) * ESZ, xo);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int p = base + u;
+        if (p >= pe) break;
+        if (p >= nend) {
+          flush();
+          while (node < nn - 1) {  // next destination with edges (monotone pointers: one step + empties)
+            ++node;
+            nstart = nend;
+            nend = s_rp[node + 1];
+            if (nend > p) break;
+          }
+          m = -INFINITY;
+          l = 0.f;
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+          get_q(node);
+        }
+        u32x4 xo;
+        M::step(a, qf, kr[u], er[u], vr[u], wt[u], m, l, acc, xo);
+        if constexpr (EOUT)
+          if (active) st16(const_cast<uint8_t*>(row_ptr16(a.e_out, rows[u])), xo);
+      }
+    }
+  };
+  if (nnz_i > 0) {
+    if constexpr (split) {
+      if (nn <= qcap) edge_loop(std::true_type{});
+      else edge_loop(std::false_type{});
+    } else {
+      edge_loop(std::true_type{});  // the node partition stages every Q row
     }
   }
   if (ps < pe) flush();
@@ -539,7 +590,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// launch helpers, one set per partition (SPLIT); the two sets are compiled in
+// launch helpers, one set per partition kind (PART); the sets are compiled in
 // separate translation units
 // ---------------------------------------------------------------------------
 
@@ -552,20 +603,21 @@ struct Problem {
   bool he, eout;
 };
 
+
 namespace detail {
 
 template <int MODE, bool HAS_E>
 constexpr int unroll() { return HAS_E ? GATTN_GATHER_U_E : GATTN_GATHER_U; }
 
-template <typename T, int D, int MODE, bool HAS_E, bool EOUT, bool SPLIT>
-constexpr auto kernel_of() { return gather_kernel<T, D, MODE, HAS_E, EOUT, unroll<MODE, HAS_E>(), SPLIT>; }
+template <typename T, int D, int MODE, bool HAS_E, bool EOUT, int PART>
+constexpr auto kernel_of() { return gather_kernel<T, D, MODE, HAS_E, EOUT, unroll<MODE, HAS_E>(), PART>; }
 
 // Workgroups of one instantiation that fit on a CU at once (queried once).
-template <typename T, int D, int MODE, bool HAS_E, bool EOUT, bool SPLIT>
+template <typename T, int D, int MODE, bool HAS_E, bool EOUT, int PART>
 int resident_per_cu() {
   static const int per_cu = [] {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kernel_of<T, D, MODE, HAS_E, EOUT, SPLIT>(), kGatherThreads,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kernel_of<T, D, MODE, HAS_E, EOUT, PART>(), kGatherThreads,
                                                      0) != hipSuccess)
       b = 1;
     return std::max(b, 1);
@@ -606,45 +658,41 @@ auto dispatch(const Problem& p, const F& f) {
   }
 }
 
-template <bool SPLIT>
+template <int PART>
 struct Resident {
   template <typename T, int D, int MODE, bool HAS_E, bool EOUT>
-  int run() const { return resident_per_cu<T, D, MODE, HAS_E, EOUT, SPLIT>(); }
+  int run() const { return resident_per_cu<T, D, MODE, HAS_E, EOUT, PART>(); }
 };
 
-template <bool SPLIT>
+template <int PART>
 struct Launch {
   const GatherArgs& ga;
   dim3 grid;
   hipStream_t s;
   template <typename T, int D, int MODE, bool HAS_E, bool EOUT>
   hipError_t run() const {
-    hipLaunchKernelGGL((kernel_of<T, D, MODE, HAS_E, EOUT, SPLIT>()), grid, dim3(kGatherThreads), 0, s, ga);
+    hipLaunchKernelGGL((kernel_of<T, D, MODE, HAS_E, EOUT, PART>()), grid, dim3(kGatherThreads), 0, s, ga);
     return hipGetLastError();
   }
 };
 
-// Defined (explicitly instantiated) in forward_gather.hip for SPLIT = false
-// and in forward_gather_split.hip for SPLIT = true.
-template <bool SPLIT>
+// Defined in forward_gather.hip (kPartNode) and forward_gather_split.hip
+// (kPartSplit).
+template <int PART>
 int resident_of(const Problem& p);
-template <bool SPLIT>
+template <int PART>
 hipError_t launch_kernels(const Problem& p, const GatherArgs& ga, dim3 grid, hipStream_t s);
 
-template <>
-int resident_of<false>(const Problem& p);
-template <>
-int resident_of<true>(const Problem& p);
-template <>
-hipError_t launch_kernels<false>(const Problem& p, const GatherArgs& ga, dim3 grid, hipStream_t s);
-template <>
-hipError_t launch_kernels<true>(const Problem& p, const GatherArgs& ga, dim3 grid, hipStream_t s);
+template <> int resident_of<kPartNode>(const Problem& p);
+template <> int resident_of<kPartSplit>(const Problem& p);
+template <> hipError_t launch_kernels<kPartNode>(const Problem& p, const GatherArgs& ga, dim3 grid, hipStream_t s);
+template <> hipError_t launch_kernels<kPartSplit>(const Problem& p, const GatherArgs& ga, dim3 grid, hipStream_t s);
 
-template <bool SPLIT>
-int resident_impl(const Problem& p) { return dispatch(p, Resident<SPLIT>{}); }
-template <bool SPLIT>
+template <int PART>
+int resident_impl(const Problem& p) { return dispatch(p, Resident<PART>{}); }
+template <int PART>
 hipError_t launch_impl(const Problem& p, const GatherArgs& ga, dim3 grid, hipStream_t s) {
-  return dispatch(p, Launch<SPLIT>{ga, grid, s});
+  return dispatch(p, Launch<PART>{ga, grid, s});
 }
 
 }  // namespace detail

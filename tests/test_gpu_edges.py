@@ -48,7 +48,8 @@ def random_inputs(n, deg_max, h, d, dtype, seed, multi=False):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("hd", [(1, 16), (3, 32), (8, 64), (2, 128)])
-def test_edge_update_with_edge_ids(gsa, dtype, hd):
+@pytest.mark.parametrize("ws", [None, True], ids=["node", "balanced"])
+def test_edge_update_with_edge_ids(gsa, dtype, hd, ws):
     # E stays in COO order; the device CSR's edge_perm addresses it
     h, d = hd
     n = 203
@@ -60,13 +61,13 @@ def test_edge_update_with_edge_ids(gsa, dtype, hd):
     ref, mag, ref_e = oracle.forward(orp, oci, *(oracle.widen(t) for t in (q, k, v, e)), mode="clipped",
                                      scale=scale, edge_ids=ope, want_mag=True, want_e_out=True)
     out, e_out = gsa.gattn_forward(rp, ci, q.cuda(), k.cuda(), v.cuda(), e.cuda(), mode="clipped", scale=scale,
-                                   path="gather", edge_ids=pe, e_out=True, validate=True)
+                                   path="gather", edge_ids=pe, e_out=True, validate=True, workspace=ws)
     check_forward(out, ref, mag, dtype)
     check_edges(e_out, ref_e, dtype)
     # the same arithmetic as E laid out by CSR position: identical bits
     e_csr = e.cuda()[pe.long()].contiguous()
     out2, e_out2 = gsa.gattn_forward(rp, ci, q.cuda(), k.cuda(), v.cuda(), e_csr, mode="clipped", scale=scale,
-                                     path="gather", e_out=True)
+                                     path="gather", e_out=True, workspace=ws)
     assert torch.equal(out, out2)
     assert torch.equal(e_out, e_out2[torch.argsort(pe.long())])
 
@@ -155,7 +156,8 @@ def oracle_aggregate(rp, ci, x, w, normalize, eps, edge_ids=None):
 @pytest.mark.parametrize("normalize", [False, True])
 @pytest.mark.parametrize("with_ids", [False, True])
 @pytest.mark.parametrize("hd", [(1, 16), (3, 32), (8, 64), (2, 128)])
-def test_aggregate_matrix(gsa, dtype, normalize, with_ids, hd):
+@pytest.mark.parametrize("ws", [None, True], ids=["node", "balanced"])
+def test_aggregate_matrix(gsa, dtype, normalize, with_ids, hd, ws):
     h, d = hd
     seed = (h * 31 + d) % 53 + (5 if normalize else 0) + (11 if with_ids else 0)
     n = 211
@@ -164,7 +166,8 @@ def test_aggregate_matrix(gsa, dtype, normalize, with_ids, hd):
     ref, mag = oracle_aggregate(rp, ci, x, w, normalize, 1e-6, ids)
     out = gsa.gattn_aggregate(torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda(), x.cuda(),
                               torch.from_numpy(w).cuda(), normalize=normalize, eps=1e-6,
-                              edge_ids=None if ids is None else torch.from_numpy(ids).cuda(), validate=True)
+                              edge_ids=None if ids is None else torch.from_numpy(ids).cuda(), validate=True,
+                              workspace=ws)
     check_forward(out, ref, mag, dtype)
 
 

@@ -77,7 +77,8 @@ def small_case(n, deg_max, h, d, dtype, mode, with_e, seed, multi=False):
 @pytest.mark.parametrize("mode", ["standard", "clipped"])
 @pytest.mark.parametrize("with_e", [False, True])
 @pytest.mark.parametrize("hd", [(1, 16), (3, 32), (8, 64), (2, 128), (8, 16), (5, 128)])
-def test_matrix_gather(gsa, dtype, mode, with_e, hd):
+@pytest.mark.parametrize("ws", [None, True], ids=["node", "balanced"])
+def test_matrix_gather(gsa, dtype, mode, with_e, hd, ws):
     h, d = hd
     seed = (h * 131 + d) % 97 + (7 if with_e else 0) + (3 if mode == "clipped" else 0)
     n = 203
@@ -86,7 +87,7 @@ def test_matrix_gather(gsa, dtype, mode, with_e, hd):
     ref, mag = oracle.forward(rp, ci, oracle.widen(q), oracle.widen(k), oracle.widen(v),
                               None if e is None else oracle.widen(e), mode=mode, scale=scale, want_mag=True)
     out = gsa.gattn_forward(torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda(), q.cuda(), k.cuda(), v.cuda(),
-                            None if e is None else e.cuda(), mode=mode, scale=scale, path="gather")
+                            None if e is None else e.cuda(), mode=mode, scale=scale, path="gather", workspace=ws)
     check_forward(out, ref, mag, dtype)
 
 
@@ -142,8 +143,9 @@ def test_empty_and_edge_cases(gsa):
         rp = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
         ci = torch.zeros(0, dtype=torch.int32, device="cuda")
         q = torch.randn(n, 2, 16, device="cuda")
-        out = gsa.gattn_forward(rp, ci, q, q.clone(), q.clone(), mode="clipped", path="gather")
-        assert out.shape == q.shape and torch.all(out == 0)
+        for ws in (None, True):
+            out = gsa.gattn_forward(rp, ci, q, q.clone(), q.clone(), mode="clipped", path="gather", workspace=ws)
+            assert out.shape == q.shape and torch.all(out == 0)
 
 
 @pytest.mark.parametrize("cfg", [2, 3])
