@@ -107,7 +107,7 @@ def algorithmic_bytes(n, nnz, h, d, s, has_e, variant="forward"):
 
 
 class Batch:
-    def __init__(self, wl, dev, host, variant="forward", partition="balanced"):
+    def __init__(self, wl, dev, host, variant="forward", partition="node"):
         import torch
         import graph_sparse_attention_amd as gsa
         self.src = host["src"].to(dev)
@@ -188,13 +188,13 @@ def cpu_baseline(wl, host, seconds, variant="forward"):
 # counters
 # ---------------------------------------------------------------------------
 
-def counters_file(path_key, config, variant="forward", partition="balanced"):
-    suffix = ("" if variant == "forward" else f"_{variant}") + ("_node" if partition == "node" and path_key == "gather" else "")
+def counters_file(path_key, config, variant="forward", partition="node"):
+    suffix = ("" if variant == "forward" else f"_{variant}") + ("_balanced" if partition == "balanced" and path_key == "gather" else "")
     return os.path.join(PROFILES, f"{'forward_gather' if path_key == 'gather' else 'forward_mfma'}"
                                   f"_config{config}{suffix}_counters.json")
 
 
-def load_traffic(path_key, config, variant="forward", partition="balanced"):
+def load_traffic(path_key, config, variant="forward", partition="node"):
     f = counters_file(path_key, config, variant, partition)
     if not os.path.exists(f):
         return None
@@ -204,7 +204,7 @@ def load_traffic(path_key, config, variant="forward", partition="balanced"):
     return d
 
 
-def ingest_counters(dirname, config, path_key, variant="forward", partition="balanced"):
+def ingest_counters(dirname, config, path_key, variant="forward", partition="node"):
     """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the forward kernel
     and of the calibration copy; scale by the copy's bytes-per-count."""
     rows = []
@@ -224,12 +224,14 @@ def ingest_counters(dirname, config, path_key, variant="forward", partition="bal
         if key is None or ctr not in ("FETCH_SIZE", "WRITE_SIZE"):
             continue
         acc.setdefault((key, ctr), []).append(val)
-    res = {k[0] + "_" + k[1]: float(np.mean(v)) for k, v in acc.items()}
+    # the calibration copy is the largest copyBuffer dispatch (the run also
+    # makes small runtime copies, which would drag an average down)
+    res = {k[0] + "_" + k[1]: float(np.max(v) if k[0] == "copy" else np.mean(v)) for k, v in acc.items()}
     copy_read = res.get("copy_FETCH_SIZE")
     copy_write = res.get("copy_WRITE_SIZE")
     fr = COPY_BYTES / (copy_read * 1024.0) if copy_read else None
     fw = COPY_BYTES / (copy_write * 1024.0) if copy_write else None
-    out = {"kernel": kern, "config": config, "variant": variant, "partition": partition,
+    out = {"kernel": kern, "config": config, "variant": variant, "partition": partition if path_key == "gather" else None,
            "kernel_source_sha256_16": src_hash(path_key),
            "fetch_kib_per_dispatch": res.get("fwd_FETCH_SIZE"), "write_kib_per_dispatch": res.get("fwd_WRITE_SIZE"),
            "copy_fetch_kib": copy_read, "copy_write_kib": copy_write, "copy_bytes_each_way": COPY_BYTES,

@@ -100,39 +100,26 @@ __global__ __launch_bounds__(kWavesPerWg * 64) void mfma_kernel(MfmaArgs a) {
 #pragma unroll
   for (int b = 0; b < NB; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K / V rows (and the mask) are loaded one tile ahead, column indices two
-  u32x4 kn[KS], vn[KS];
-  uint32_t bits_n = 0;
-  int32_t col_b = -1;
-  uint32_t mask_b = 0;
-  auto load_kv = [&](int32_t col, uint32_t mask) {
-    const bool col_ok = (uint32_t)col < (uint32_t)a.n;
-    const int64_t src_off = (int64_t)(col_ok ? col : 0) * rowstride + (int64_t)h * D;
+  // Loads are issued with no branch around them (tile indices are clamped to
+  // the last tile, and a padding column reads row 0, whose V is zeroed
+  // before use) and land in register sets that take turns (the loop is
+  // unrolled), so no register copy makes a tile wait for the prefetches
+  // issued after it.
+  const int64_t clast = max(c1 - 16, c0);
+  auto load_kv = [&](int32_t col, u32x4* kk, u32x4* vv) {
+    const int64_t src_off = (int64_t)((uint32_t)col < (uint32_t)a.n ? col : 0) * rowstride + (int64_t)h * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      kn[s] = col_ok ? ld16(a.k + src_off + 32 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u};
-      vn[s] = col_ok ? ld16(a.v + src_off + 32 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+      kk[s] = ld16(a.k + src_off + 32 * s + 8 * g);
+      vv[s] = ld16(a.v + src_off + 32 * s + 8 * g);
     }
-    bits_n = mask >> (4 * g);
   };
-  if (c0 < c1) load_kv(a.win_cols[c0 + r], a.tile_mask[c0 + r]);
-  if (c0 + 16 < c1) {
-    col_b = a.win_cols[c0 + 16 + r];
-    mask_b = a.tile_mask[c0 + 16 + r];
-  }
-
-  for (int64_t c = c0; c < c1; c += 16) {
-    u32x4 kf[KS], vf[KS];
+  // tile at column c with rows (kf, vf), column id col and row mask `mask`
+  auto tile = [&](u32x4* kf, u32x4* vf, int32_t col, uint32_t mask) {
+    const uint32_t bits = mask >> (4 * g);
+    if ((uint32_t)col >= (uint32_t)a.n) {  // padding column: no edge, V row zero
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      kf[s] = kn[s];
-      vf[s] = vn[s];
-    }
-    const uint32_t bits = bits_n;
-    if (c + 16 < c1) load_kv(col_b, mask_b);
-    if (c + 32 < c1) {
-      col_b = a.win_cols[c + 32 + r];
-      mask_b = a.tile_mask[c + 32 + r];
+      for (int s = 0; s < KS; ++s) vf[s] = u32x4{0u, 0u, 0u, 0u};
     }
 
     // SDDMM on the matrix cores
@@ -188,6 +175,30 @@ __global__ __launch_bounds__(kWavesPerWg * 64) void mfma_kernel(MfmaArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  if (c0 < c1) {
+    // two register sets in turn: while tile t computes from one, the rows of
+    // tile t + 1 are in flight into the other; column ids and masks are read
+    // one tile before their rows
+    u32x4 ka[KS], va[KS], kb[KS], vb[KS];
+    int32_t col_a = a.win_cols[c0 + r], col_b = a.win_cols[min(c0 + 16, clast) + r];
+    uint32_t mask_a = a.tile_mask[c0 + r], mask_b = a.tile_mask[min(c0 + 16, clast) + r];
+    load_kv(col_a, ka, va);
+    for (int64_t c = c0; c < c1; c += 32) {
+      load_kv(col_b, kb, vb);
+      const int32_t col_c = col_a;
+      const uint32_t mask_c = mask_a;
+      col_a = a.win_cols[min(c + 32, clast) + r];
+      mask_a = a.tile_mask[min(c + 32, clast) + r];
+      tile(ka, va, col_c, mask_c);
+      if (c + 16 >= c1) break;
+      load_kv(col_a, ka, va);
+      const int32_t col_d = col_b;
+      const uint32_t mask_d = mask_b;
+      col_b = a.win_cols[min(c + 48, clast) + r];
+      mask_b = a.tile_mask[min(c + 48, clast) + r];
+      tile(kb, vb, col_d, mask_d);
+    }
   }
 
   // O[row r][d = 16b + 4g + i] = O^T[d][r] / l  (row without edges -> 0)

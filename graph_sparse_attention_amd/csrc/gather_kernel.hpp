@@ -297,20 +297,39 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
   const int qcap = AGG ? 0 : kQLdsBytes / qrow;  // rows whose Q is staged in LDS
 
   // ---- phase 0: row pointers and Q rows into LDS (one coalesced pass); a
-  // range that starts or ends inside a row starts or ends at the cut edge
-  for (int t = tid; t <= nn; t += kGatherThreads) {
-    int v = min(max(a.row_ptr[n0 + t], 0), nnz_i);
+  // range that starts or ends inside a row starts or ends at the cut edge.
+  // The first batch of both is loaded before anything is stored, so that the
+  // two loads are in flight together.
+  constexpr int kQB = 4;  // Q chunks per thread in the first batch
+  const int qn = AGG ? 0 : min(nn, qcap) * chunks;
+  auto q_src = [&](int t) {
+    const int li = t / chunks, c = t - li * chunks;
+    return a.q + ((int64_t)(n0 + li) * rowstride + (int64_t)hb * a.HB * D + c * VEC) * ESZ;
+  };
+  auto q_dst = [&](int t) {
+    const int li = t / chunks, c = t - li * chunks;
+    return reinterpret_cast<u32x4*>(s_q + li * qrow + c * 16);
+  };
+  auto rp_val = [&](int t, int v) {
+    v = min(max(v, 0), nnz_i);
     if (split && t == nn) v = s_cut[4];
     if (split && t == 0) v = s_cut[1];
-    s_rp[t] = v;
+    return v;
+  };
+  {
+    // addresses clamped into range: no branch around a load, so no merge of
+    // its register that would wait for it before the next load is issued
+    const int r0 = a.row_ptr[n0 + min(tid, nn)];
+    u32x4 qv[kQB];
+#pragma unroll
+    for (int j = 0; j < kQB; ++j) qv[j] = qn > 0 ? ld16(q_src(min(tid + j * kGatherThreads, qn - 1))) : u32x4{0u, 0u, 0u, 0u};
+    if (tid <= nn) s_rp[tid] = rp_val(tid, r0);
+#pragma unroll
+    for (int j = 0; j < kQB; ++j)
+      if (tid + j * kGatherThreads < qn) *q_dst(tid + j * kGatherThreads) = qv[j];
   }
-  if constexpr (!AGG) {
-    for (int t = tid; t < min(nn, qcap) * chunks; t += kGatherThreads) {
-      const int li = t / chunks, c = t - li * chunks;
-      *reinterpret_cast<u32x4*>(s_q + li * qrow + c * 16) =
-          ld16(a.q + ((int64_t)(n0 + li) * rowstride + (int64_t)hb * a.HB * D + c * VEC) * ESZ);
-    }
-  }
+  for (int t = tid + kGatherThreads; t <= nn; t += kGatherThreads) s_rp[t] = rp_val(t, a.row_ptr[n0 + t]);
+  for (int t = tid + kQB * kGatherThreads; t < qn; t += kGatherThreads) *q_dst(t) = ld16(q_src(t));
   __syncthreads();
 
   for (int t = tid; t < nn * chunks; t += kGatherThreads) {
