@@ -56,6 +56,7 @@ KERNEL_SRC = {"gather": ["graph_sparse_attention_amd/csrc/gather_kernel.hpp",
                          "graph_sparse_attention_amd/csrc/forward_gather.hip",
                          "graph_sparse_attention_amd/csrc/forward_gather_split.hip"],
               "mfma": ["graph_sparse_attention_amd/csrc/forward_mfma.hip"]}
+KERNEL_SRC["hybrid"] = KERNEL_SRC["mfma"] + KERNEL_SRC["gather"]
 COPY_BYTES = 512 << 20      # calibration copy for the traffic counters
 VARIANTS = {"forward": "gattn_forward", "e_out": "gattn_forward + edge update",
             "edge_ids": "gattn_forward, E through edge ids", "aggregate": "gattn_aggregate (normalized)"}
@@ -66,8 +67,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", type=int, default=2)
-    p.add_argument("--path", default="auto", choices=["auto", "gather", "mfma"])
+    p.add_argument("--config", type=int, default=2,
+                   help="1-5: the benchmark configurations; 6: the mixed-density batch of the hybrid dispatch")
+    p.add_argument("--path", default="auto", choices=["auto", "gather", "mfma", "hybrid"])
+    p.add_argument("--min-density", type=float, default=0.25, help="hybrid path: tile density of an MFMA window")
     p.add_argument("--variant", default="forward", choices=list(VARIANTS))
     p.add_argument("--partition", default="node", choices=["balanced", "node"],
                    help="gather path: edge-balanced workgroups with cut heavy rows (workspace) or equal node counts")
@@ -119,6 +122,7 @@ class Batch:
         self.e_out = torch.empty_like(self.e) if host.get("e_out") and self.e is not None else None
         self.csr = gsa.CsrBuilder(wl.num_nodes, wl.nnz, dev)
         self.rw = None
+        self.hy = None
         self.ws = None
         if partition == "balanced":
             rp, ci = self.csr.row_ptr, self.csr.col_idx
@@ -190,8 +194,7 @@ def cpu_baseline(wl, host, seconds, variant="forward"):
 
 def counters_file(path_key, config, variant="forward", partition="node"):
     suffix = ("" if variant == "forward" else f"_{variant}") + ("_balanced" if partition == "balanced" and path_key == "gather" else "")
-    return os.path.join(PROFILES, f"{'forward_gather' if path_key == 'gather' else 'forward_mfma'}"
-                                  f"_config{config}{suffix}_counters.json")
+    return os.path.join(PROFILES, f"forward_{path_key}_config{config}{suffix}_counters.json")
 
 
 def load_traffic(path_key, config, variant="forward", partition="node"):
@@ -214,19 +217,26 @@ def ingest_counters(dirname, config, path_key, variant="forward", partition="nod
             rows += list(csv.DictReader(fh))
     if not rows:
         raise SystemExit(f"no counter CSV under {dirname}")
-    kern = "gather_kernel" if path_key == "gather" else "mfma_kernel"
+    kerns = {"gather": ["gather_kernel"], "mfma": ["mfma_kernel"], "hybrid": ["mfma_kernel", "gather_kernel"]}[path_key]
+    kern = " + ".join(kerns)
     acc = {}
     for r in rows:
         name = r.get("Kernel_Name", "")
         ctr = r.get("Counter_Name", "")
         val = float(r.get("Counter_Value", "nan"))
-        key = "copy" if "copyBuffer" in name else ("fwd" if kern in name else None)
+        key = "copy" if "copyBuffer" in name else next((k for k in kerns if k in name), None)
         if key is None or ctr not in ("FETCH_SIZE", "WRITE_SIZE"):
             continue
         acc.setdefault((key, ctr), []).append(val)
     # the calibration copy is the largest copyBuffer dispatch (the run also
-    # makes small runtime copies, which would drag an average down)
-    res = {k[0] + "_" + k[1]: float(np.max(v) if k[0] == "copy" else np.mean(v)) for k, v in acc.items()}
+    # makes small runtime copies, which would drag an average down); one
+    # launch of the op is one dispatch of each of its kernels
+    res = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        if ("copy", ctr) in acc:
+            res["copy_" + ctr] = float(np.max(acc[("copy", ctr)]))
+        if all((k, ctr) in acc for k in kerns):
+            res["fwd_" + ctr] = float(sum(np.mean(acc[(k, ctr)]) for k in kerns))
     copy_read = res.get("copy_FETCH_SIZE")
     copy_write = res.get("copy_WRITE_SIZE")
     fr = COPY_BYTES / (copy_read * 1024.0) if copy_read else None
@@ -254,7 +264,7 @@ def main():
         sys.exit(2)
     import workloads as W
     if args.ingest_counters:
-        path_key = "mfma" if args.path == "mfma" else "gather"
+        path_key = args.path if args.path in ("mfma", "hybrid") else "gather"
         ingest_counters(args.ingest_counters, args.config, path_key, args.variant, args.partition)
         return
 
@@ -278,7 +288,15 @@ def main():
             gsa.gattn_forward(rp, ci, b.q, b.k, b.v, b.e, mode=wl.mode, scale=wl.scale, clip=wl.clip, eps=wl.eps,
                               path=args.path, rw=b.rw, out=b.out,
                               edge_ids=pe if args.variant == "edge_ids" else None, e_out=b.e_out,
-                              workspace=b.ws)
+                              workspace=b.ws, hybrid=b.hy)
+
+    def plans(b, rp, ci):
+        """Row windows (and the hybrid plan) once per graph: they synchronize,
+        so they are built in the warmup, never inside the timed region."""
+        if b.rw is None:
+            b.rw = gsa.gattn_build_rowwindows(rp, ci, wl.num_nodes)
+        if args.path == "hybrid" and b.hy is None:
+            b.hy = gsa.gattn_build_hybrid(rp, ci, b.rw, b.q, min_density=args.min_density)
 
     if args.counters_run:
         a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -289,7 +307,8 @@ def main():
         torch.cuda.synchronize()
         bt = Batch(wl, dev, host, args.variant, args.partition)
         rp, ci, pe = bt.csr(bt.src, bt.dst)
-        bt.rw = gsa.gattn_build_rowwindows(rp, ci, wl.num_nodes) if args.path == "mfma" else None
+        if args.path in ("mfma", "hybrid"):
+            plans(bt, rp, ci)
         for _ in range(5):
             run_op(bt, rp, ci, pe)
         torch.cuda.synchronize()
@@ -300,7 +319,7 @@ def main():
     R = max(2, min(16, math.ceil(3 * MALL_BYTES / max(batch_bytes(wl, es, args.variant), 1)) + 1))
     print(f"# {wl.name}: N={wl.num_nodes} nnz={wl.nnz}; {R} rotating batches", file=sys.stderr, flush=True)
     batches = [Batch(wl, dev, host, args.variant, args.partition) for _ in range(R)]
-    use_rw = args.variant == "forward" and (args.path == "mfma" or (
+    use_rw = args.variant == "forward" and (args.path in ("mfma", "hybrid") or (
         args.path == "auto" and wl.dtype != "f32" and wl.mode == "standard" and not wl.has_e))
 
     def step(i, ev=None):
@@ -309,8 +328,7 @@ def main():
             ev[0].record()
         rp, ci, pe = b.csr(b.src, b.dst)
         if use_rw:
-            if b.rw is None:          # row windows once per graph (they synchronize; never inside timing)
-                b.rw = gsa.gattn_build_rowwindows(rp, ci, wl.num_nodes)
+            plans(b, rp, ci)
         if ev is not None:
             ev[1].record()
         run_op(b, rp, ci, pe)
@@ -324,7 +342,8 @@ def main():
     for b in batches:
         assert int(b.csr.status.item()) == 0, "bad graph"
     path = "gather" if args.variant == "aggregate" else gsa.gattn_forward_path(batches[0].csr.row_ptr, batches[0].csr.col_idx, batches[0].q, batches[0].k,
-                                  batches[0].v, batches[0].e, mode=wl.mode, path=args.path, rw=batches[0].rw)
+                                  batches[0].v, batches[0].e, mode=wl.mode, path=args.path, rw=batches[0].rw,
+                                  hybrid=batches[0].hy)
 
     # host enqueue rate, to size the sleep that keeps the GPU backlogged
     t0 = time.perf_counter()
@@ -353,12 +372,12 @@ def main():
     nnz = wl.nnz
     bmin = algorithmic_bytes(wl.num_nodes, nnz, wl.heads, wl.head_dim, es, wl.has_e, args.variant)
     achieved = bmin / (fwd_ms * 1e-3) / 1e9
-    pk = "mfma" if path == "mfma" else "gather"
+    pk = path if path in ("mfma", "hybrid") else "gather"
     tr = load_traffic(pk, args.config, args.variant, args.partition)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": (round(tr["hbm_bytes_per_launch"]) if tr and tr.get("hbm_bytes_per_launch") else None),
-                "kernel": "gather_kernel" if pk == "gather" else "mfma_kernel",
+                "kernel": {"gather": "gather_kernel", "mfma": "mfma_kernel", "hybrid": "mfma_kernel + gather_kernel"}[pk],
                 "algorithmic_bytes_per_launch": bmin, "bytes_per_edge": round(bmin / nnz, 2),
                 "kernel_ms": round(fwd_ms, 5), "kernel_ms_min": round(float(fwd_ms_all.min()), 5)}
     res = {"metric": METRIC, "value": round(nnz / (ms_per_step * 1e-3) / 1e9, 4), "unit": "GEdges/s",

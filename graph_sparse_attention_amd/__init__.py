@@ -7,7 +7,8 @@ current stream.  Names follow the C ABI in ``include/gattn.h``:
     gattn_build_csr(src, dst, num_nodes)            -> (row_ptr, col_idx, edge_perm)
     gattn_build_rowwindows(row_ptr, col_idx, n)     -> RowWindows
     gattn_forward(row_ptr, col_idx, q, k, v, ...)   -> out [N, H, D]  (, e_out)
-    gattn_forward_path(...)                         -> "gather" | "mfma"
+    gattn_build_hybrid(row_ptr, col_idx, rw, q)     -> Hybrid (per-window plan)
+    gattn_forward_path(...)                         -> "gather" | "mfma" | "hybrid"
     gattn_aggregate(row_ptr, col_idx, x, w, ...)    -> out [N, H, D]
 
 Every call raises if ``libgattn.so`` is missing or stale: there is no
@@ -31,13 +32,13 @@ GATTN_OK, GATTN_ERR_INVALID_VALUE, GATTN_ERR_UNSUPPORTED, GATTN_ERR_BAD_GRAPH, \
     GATTN_ERR_DUPLICATE_EDGE, GATTN_ERR_BUFFER_TOO_SMALL, GATTN_ERR_HIP = range(7)
 GATTN_F32, GATTN_F16, GATTN_BF16 = range(3)
 GATTN_SOFTMAX_STANDARD, GATTN_SOFTMAX_CLIPPED = range(2)
-GATTN_PATH_AUTO, GATTN_PATH_GATHER, GATTN_PATH_MFMA = range(3)
+GATTN_PATH_AUTO, GATTN_PATH_GATHER, GATTN_PATH_MFMA, GATTN_PATH_HYBRID = range(4)
 GATTN_FLAG_VALIDATE = 1
 
 _DTYPES = {torch.float32: GATTN_F32, torch.float16: GATTN_F16, torch.bfloat16: GATTN_BF16}
 _MODES = {"standard": GATTN_SOFTMAX_STANDARD, "clipped": GATTN_SOFTMAX_CLIPPED}
-_PATHS = {"auto": GATTN_PATH_AUTO, "gather": GATTN_PATH_GATHER, "mfma": GATTN_PATH_MFMA}
-_PATH_NAMES = {GATTN_PATH_GATHER: "gather", GATTN_PATH_MFMA: "mfma"}
+_PATHS = {"auto": GATTN_PATH_AUTO, "gather": GATTN_PATH_GATHER, "mfma": GATTN_PATH_MFMA, "hybrid": GATTN_PATH_HYBRID}
+_PATH_NAMES = {GATTN_PATH_GATHER: "gather", GATTN_PATH_MFMA: "mfma", GATTN_PATH_HYBRID: "hybrid"}
 
 
 class GattnError(RuntimeError):
@@ -51,6 +52,11 @@ class _RowWindows(ctypes.Structure):
                 ("win_col_ptr", ctypes.c_void_p), ("win_cols", ctypes.c_void_p), ("tile_mask", ctypes.c_void_p)]
 
 
+class _Hybrid(ctypes.Structure):
+    _fields_ = [("num_dense", ctypes.c_int32), ("num_ranges", ctypes.c_int32), ("range_rows", ctypes.c_int32),
+                ("dense_windows", ctypes.c_void_p), ("ranges", ctypes.c_void_p)]
+
+
 class _ForwardArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("num_nodes", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("nnz", ctypes.c_int64),
@@ -60,7 +66,8 @@ class _ForwardArgs(ctypes.Structure):
                 ("scale", ctypes.c_float), ("clip_lo", ctypes.c_float), ("clip_hi", ctypes.c_float),
                 ("eps", ctypes.c_float), ("path", ctypes.c_int), ("rw", ctypes.POINTER(_RowWindows)),
                 ("flags", ctypes.c_uint32), ("edge_ids", ctypes.c_void_p), ("e_out", ctypes.c_void_p),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("hybrid", ctypes.POINTER(_Hybrid))]
 
 
 class _AggregateArgs(ctypes.Structure):
@@ -103,10 +110,11 @@ def _load():
     L.gattn_forward_path.argtypes = [ctypes.POINTER(_ForwardArgs), ctypes.POINTER(ctypes.c_int)]
     L.gattn_aggregate.argtypes = [ctypes.POINTER(_AggregateArgs), vp]
     L.gattn_forward_workspace.argtypes = [ctypes.POINTER(_ForwardArgs), sz]
+    L.gattn_build_hybrid.argtypes = [ctypes.POINTER(_ForwardArgs), ctypes.c_float, vp, vp, ctypes.POINTER(_Hybrid), vp]
     L.gattn_aggregate_workspace.argtypes = [ctypes.POINTER(_AggregateArgs), sz]
     for f in (L.gattn_build_csr_workspace, L.gattn_build_csr, L.gattn_build_rowwindows_workspace,
               L.gattn_build_rowwindows, L.gattn_forward, L.gattn_forward_path, L.gattn_aggregate,
-              L.gattn_forward_workspace, L.gattn_aggregate_workspace):
+              L.gattn_forward_workspace, L.gattn_aggregate_workspace, L.gattn_build_hybrid):
         f.restype = st
     return L
 
@@ -233,8 +241,45 @@ def gattn_build_rowwindows(row_ptr: torch.Tensor, col_idx: torch.Tensor, num_nod
     return RowWindows(num_nodes, wcp, cols[:C], mask[:C].view(C // 16, 16) if C else mask[:0].view(0, 16))
 
 
+@dataclasses.dataclass
+class Hybrid:
+    """Per-window dispatch plan of gattn_build_hybrid (device lists)."""
+    num_dense: int
+    num_ranges: int
+    range_rows: int
+    dense_windows: torch.Tensor   # int32 [ceil(N/16)], first num_dense used
+    ranges: torch.Tensor          # int32 [2N], first 2*num_ranges used
+
+    def _struct(self):
+        return _Hybrid(self.num_dense, self.num_ranges, self.range_rows, self.dense_windows.data_ptr(),
+                       self.ranges.data_ptr())
+
+
+def gattn_build_hybrid(row_ptr: torch.Tensor, col_idx: torch.Tensor, rw: RowWindows, q: torch.Tensor,
+                       min_density: float = 0.25) -> Hybrid:
+    """Row windows whose tile density (edges / (16 * columns)) is at least
+    min_density go to the MFMA path, the other rows to the gather path, in
+    ranges sized like its workgroups.  q gives the geometry (N, H, D, dtype);
+    the plan is for the standard mode without an edge tensor."""
+    row_ptr, col_idx = _i32(row_ptr, "row_ptr"), _i32(col_idx, "col_idx")
+    if q.dim() != 3 or not q.is_cuda or q.dtype not in _DTYPES:
+        raise ValueError("q must be an [N, H, D] GPU tensor")
+    N = q.shape[0]
+    W = (N + 15) // 16
+    dev = q.device
+    dense = torch.empty(max(W, 1), dtype=torch.int32, device=dev)
+    ranges = torch.empty(max(2 * N, 2), dtype=torch.int32, device=dev)
+    a, keep = _forward_args(row_ptr, col_idx, q, q, q, None, None, "standard", None, (-5.0, 5.0), 1e-6, "hybrid", rw,
+                            False)
+    plan = _Hybrid()
+    _check(_lib.gattn_build_hybrid(ctypes.byref(a), float(min_density), _ptr(dense), _ptr(ranges), ctypes.byref(plan),
+                                   _stream(dev)), "gattn_build_hybrid")
+    del keep
+    return Hybrid(plan.num_dense, plan.num_ranges, plan.range_rows, dense, ranges)
+
+
 def _forward_args(row_ptr, col_idx, q, k, v, e, out, mode, scale, clip, eps, path, rw, validate,
-                  edge_ids=None, e_out=None):
+                  edge_ids=None, e_out=None, hybrid=None):
     N, H, D = q.shape
     a = _ForwardArgs()
     a.struct_size = ctypes.sizeof(_ForwardArgs)
@@ -250,10 +295,13 @@ def _forward_args(row_ptr, col_idx, q, k, v, e, out, mode, scale, clip, eps, pat
     a.clip_lo, a.clip_hi = clip
     a.eps = eps
     a.path = _PATHS[path]
-    keep = None
+    keep = []
     if rw is not None:
-        keep = rw._struct()
-        a.rw = ctypes.pointer(keep)
+        keep.append(rw._struct())
+        a.rw = ctypes.pointer(keep[-1])
+    if hybrid is not None:
+        keep.append(hybrid._struct())
+        a.hybrid = ctypes.pointer(keep[-1])
     a.flags = GATTN_FLAG_VALIDATE if validate else 0
     a.edge_ids = None if edge_ids is None else edge_ids.data_ptr()
     a.e_out = None if e_out is None else e_out.data_ptr()
@@ -312,7 +360,8 @@ def gattn_forward(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch.Tensor,
                   e: Optional[torch.Tensor] = None, mode: str = "standard", scale: Optional[float] = None,
                   clip=(-5.0, 5.0), eps: float = 1e-6, path: str = "auto", rw: Optional[RowWindows] = None,
                   out: Optional[torch.Tensor] = None, validate: bool = False,
-                  edge_ids: Optional[torch.Tensor] = None, e_out=None, workspace=None):
+                  edge_ids: Optional[torch.Tensor] = None, e_out=None, workspace=None,
+                  hybrid: Optional[Hybrid] = None):
     """Fused SDDMM -> softmax -> SpMM over the CSR; q/k/v [N, H, D]; e
     [nnz, H, D] by CSR position (or row edge_ids[p] for position p) or None.
     Returns out [N, H, D]; with e_out (True, or an [nnz, H, D] tensor) the
@@ -320,7 +369,9 @@ def gattn_forward(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch.Tensor,
     workspace: None (default) runs the node partition (equal destination
     counts per workgroup); True allocates the balanced-partition workspace
     and a uint8 tensor supplies it (equal edge shares, heavy rows cut across
-    workgroups: for graphs whose hubs hold many times a workgroup's share)."""
+    workgroups: for graphs whose hubs hold many times a workgroup's share).
+    hybrid (with rw): a gattn_build_hybrid plan for path "hybrid" (or
+    "auto"): dense row windows on the MFMA path, the other rows gathered."""
     row_ptr, col_idx = _i32(row_ptr, "row_ptr"), _i32(col_idx, "col_idx")
     if q.dim() != 3 or not q.is_contiguous() or not q.is_cuda:
         raise ValueError("q must be a contiguous [N, H, D] GPU tensor")
@@ -344,7 +395,7 @@ def gattn_forward(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch.Tensor,
     else:
         _check_node_tensor(out, "out", q)
     a, keep = _forward_args(row_ptr, col_idx, q, k, v, e, out, mode, scale, clip, eps, path, rw, validate,
-                            edge_ids, e_out if want_e_out else None)
+                            edge_ids, e_out if want_e_out else None, hybrid)
     ws = _attach_workspace(a, _lib.gattn_forward_workspace, workspace, q.device, "gattn_forward_workspace")
     _check(_lib.gattn_forward(ctypes.byref(a), _stream(q.device)), "gattn_forward")
     del keep, ws
@@ -352,8 +403,9 @@ def gattn_forward(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch.Tensor,
 
 
 def gattn_forward_path(row_ptr, col_idx, q, k, v, e=None, mode="standard", path="auto",
-                       rw: Optional[RowWindows] = None) -> str:
-    a, keep = _forward_args(row_ptr, col_idx, q, k, v, e, None, mode, None, (-5.0, 5.0), 1e-6, path, rw, False)
+                       rw: Optional[RowWindows] = None, hybrid: Optional[Hybrid] = None) -> str:
+    a, keep = _forward_args(row_ptr, col_idx, q, k, v, e, None, mode, None, (-5.0, 5.0), 1e-6, path, rw, False,
+                            hybrid=hybrid)
     res = ctypes.c_int(0)
     _check(_lib.gattn_forward_path(ctypes.byref(a), ctypes.byref(res)), "gattn_forward_path")
     del keep
@@ -397,6 +449,6 @@ def gattn_aggregate(row_ptr: torch.Tensor, col_idx: torch.Tensor, x: torch.Tenso
     return out
 
 
-__all__ = ["gattn_build_csr", "gattn_build_rowwindows", "gattn_forward", "gattn_forward_path", "gattn_aggregate",
+__all__ = ["gattn_build_csr", "gattn_build_rowwindows", "gattn_build_hybrid", "gattn_forward", "gattn_forward_path", "gattn_aggregate",
            "gattn_forward_workspace", "gattn_aggregate_workspace",
-           "gattn_status_string", "gattn_abi_version", "CsrBuilder", "RowWindows", "GattnError", "LIB_PATH"]
+           "gattn_status_string", "gattn_abi_version", "CsrBuilder", "RowWindows", "Hybrid", "GattnError", "LIB_PATH"]

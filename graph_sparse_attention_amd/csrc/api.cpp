@@ -13,7 +13,8 @@
 using namespace gattn;
 
 // the Python binding mirrors these layouts with ctypes
-static_assert(sizeof(gattn_forward_args) == 160, "gattn_forward_args layout");
+static_assert(sizeof(gattn_forward_args) == 168, "gattn_forward_args layout");
+static_assert(sizeof(gattn_hybrid) == 32, "gattn_hybrid layout");
 static_assert(sizeof(gattn_aggregate_args) == 104, "gattn_aggregate_args layout");
 static_assert(sizeof(gattn_rowwindows) == 40, "gattn_rowwindows layout");
 
@@ -38,7 +39,8 @@ gattn_status check_forward(const gattn_forward_args* a, bool launch) {
   if (a->num_nodes < 0 || a->num_heads < 1 || a->nnz < 0 || a->nnz > INT32_MAX) return GATTN_ERR_INVALID_VALUE;
   if (a->dtype != GATTN_F32 && a->dtype != GATTN_F16 && a->dtype != GATTN_BF16) return GATTN_ERR_INVALID_VALUE;
   if (a->mode != GATTN_SOFTMAX_STANDARD && a->mode != GATTN_SOFTMAX_CLIPPED) return GATTN_ERR_INVALID_VALUE;
-  if (a->path != GATTN_PATH_AUTO && a->path != GATTN_PATH_GATHER && a->path != GATTN_PATH_MFMA)
+  if (a->path != GATTN_PATH_AUTO && a->path != GATTN_PATH_GATHER && a->path != GATTN_PATH_MFMA &&
+      a->path != GATTN_PATH_HYBRID)
     return GATTN_ERR_INVALID_VALUE;
   if (a->flags & ~GATTN_FLAG_VALIDATE) return GATTN_ERR_INVALID_VALUE;
   if (!(a->scale > 0.f) || !(a->scale < INFINITY)) return GATTN_ERR_INVALID_VALUE;
@@ -128,9 +130,32 @@ gattn_status check_rw(const gattn_forward_args* a) {
   return GATTN_OK;
 }
 
+// A hybrid plan: counts within the graph's windows and rows, ranges no
+// larger than the gather path can stage, arrays present when counts are not 0.
+gattn_status check_hybrid(const gattn_forward_args* a) {
+  const gattn_hybrid* hy = a->hybrid;
+  if (!hy) return GATTN_ERR_INVALID_VALUE;
+  const int32_t W = (a->num_nodes + 15) / 16;
+  if (hy->num_dense < 0 || hy->num_dense > W || hy->num_ranges < 0 || hy->num_ranges > a->num_nodes)
+    return GATTN_ERR_INVALID_VALUE;
+  if ((hy->num_dense > 0 && !hy->dense_windows) || (hy->num_ranges > 0 && !hy->ranges)) return GATTN_ERR_INVALID_VALUE;
+  if (!aligned(hy->dense_windows, 4) || !aligned(hy->ranges, 4)) return GATTN_ERR_INVALID_VALUE;
+  if (hy->num_ranges > 0 && (hy->range_rows < 1 || hy->range_rows > gather_max_range_rows(*a)))
+    return GATTN_ERR_INVALID_VALUE;
+  return GATTN_OK;
+}
+
 gattn_status resolve(const gattn_forward_args* a, gattn_path* out) {
   const bool mf = mfma_supported(*a);
   if (a->path == GATTN_PATH_GATHER) { *out = GATTN_PATH_GATHER; return GATTN_OK; }
+  if (a->path == GATTN_PATH_HYBRID || (a->path == GATTN_PATH_AUTO && a->hybrid && mf)) {
+    if (!mf) return GATTN_ERR_UNSUPPORTED;
+    gattn_status st = check_rw(a);
+    if (st == GATTN_OK) st = check_hybrid(a);
+    if (st != GATTN_OK) return st;
+    *out = GATTN_PATH_HYBRID;
+    return GATTN_OK;
+  }
   if (a->path == GATTN_PATH_MFMA) {
     if (!mf) return GATTN_ERR_UNSUPPORTED;
     gattn_status st = check_rw(a);
@@ -275,6 +300,76 @@ gattn_status gattn_forward_path(const gattn_forward_args* args, gattn_path* path
   return resolve(args, path);
 }
 
+gattn_status gattn_build_hybrid(const gattn_forward_args* args, float min_density, int32_t* dense_windows,
+                                int32_t* ranges, gattn_hybrid* plan, hipStream_t stream) {
+  try {
+    if (!plan) return GATTN_ERR_INVALID_VALUE;
+    gattn_status st = check_forward(args, false);
+    if (st != GATTN_OK) return st;
+    if (!mfma_supported(*args)) return GATTN_ERR_UNSUPPORTED;
+    if ((st = check_rw(args)) != GATTN_OK) return st;
+    if (!(min_density >= 0.f) || !(min_density < INFINITY)) return GATTN_ERR_INVALID_VALUE;
+    const int32_t n = args->num_nodes, W = (n + 15) / 16;
+    if (n > 0 && (!dense_windows || !ranges)) return GATTN_ERR_INVALID_VALUE;
+    if (!aligned(dense_windows, 4) || !aligned(ranges, 4)) return GATTN_ERR_INVALID_VALUE;
+    *plan = gattn_hybrid{0, 0, 1, dense_windows, ranges};
+    if (n == 0) return GATTN_OK;
+    // one flag per window on the device (into dense_windows), read back
+    if (hipError_t e = launch_hybrid_flags(n, args->row_ptr, args->rw->win_col_ptr, W, min_density, dense_windows,
+                                           stream);
+        e != hipSuccess)
+      return GATTN_ERR_HIP;
+    std::vector<int32_t> flags((size_t)W);
+    if (hipMemcpyAsync(flags.data(), dense_windows, flags.size() * 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+      return GATTN_ERR_HIP;
+    // the dense list, and the sparse rows cut into ranges of consecutive rows
+    std::vector<int32_t> dense, rng;
+    int32_t sparse_rows = 0;
+    int64_t sparse_nnz = 0;
+    for (int32_t w = 0; w < W; ++w) {
+      if (flags[w] < 0) {
+        dense.push_back(w);
+      } else {
+        sparse_rows += std::min(16, n - 16 * w);
+        sparse_nnz += flags[w];
+      }
+    }
+    const int32_t R = sparse_rows > 0 ? std::max(1, std::min(hybrid_rows_per_range(*args, sparse_rows, sparse_nnz),
+                                                             gather_max_range_rows(*args)))
+                                      : 1;
+    int32_t start = -1, count = 0;
+    for (int32_t w = 0; w <= W; ++w) {
+      const bool sparse = w < W && flags[w] >= 0;
+      for (int32_t r = 16 * w; sparse && r < std::min(16 * w + 16, n); ++r) {
+        if (count > 0 && (start + count != r || count == R)) {
+          rng.push_back(start);
+          rng.push_back(count);
+          count = 0;
+        }
+        if (count == 0) start = r;
+        ++count;
+      }
+      if (!sparse && count > 0) {
+        rng.push_back(start);
+        rng.push_back(count);
+        count = 0;
+      }
+    }
+    if (!dense.empty() && hipMemcpyAsync(dense_windows, dense.data(), dense.size() * 4, hipMemcpyHostToDevice,
+                                         stream) != hipSuccess)
+      return GATTN_ERR_HIP;
+    if (!rng.empty() &&
+        hipMemcpyAsync(ranges, rng.data(), rng.size() * 4, hipMemcpyHostToDevice, stream) != hipSuccess)
+      return GATTN_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return GATTN_ERR_HIP;
+    *plan = gattn_hybrid{(int32_t)dense.size(), (int32_t)(rng.size() / 2), R, dense_windows, ranges};
+    return GATTN_OK;
+  } catch (...) {
+    return GATTN_ERR_HIP;
+  }
+}
+
 gattn_status gattn_forward_workspace(const gattn_forward_args* args, size_t* bytes) {
   try {
     if (!bytes) return GATTN_ERR_INVALID_VALUE;
@@ -312,7 +407,12 @@ gattn_status gattn_forward(const gattn_forward_args* args, hipStream_t stream) {
                                stream)) != GATTN_OK)
         return st;
     }
-    if (path == GATTN_PATH_MFMA) return from_hip(launch_forward_mfma(*args, stream));
+    if (path == GATTN_PATH_MFMA) return from_hip(launch_forward_mfma(*args, nullptr, 0, stream));
+    if (path == GATTN_PATH_HYBRID) {
+      const gattn_hybrid* hy = args->hybrid;
+      if ((st = from_hip(launch_forward_mfma(*args, hy->dense_windows, hy->num_dense, stream))) != GATTN_OK) return st;
+      return from_hip(launch_forward_gather_ranges(*args, hy->ranges, hy->num_ranges, hy->range_rows, stream));
+    }
     if (args->workspace && args->workspace_bytes < forward_gather_workspace_bytes(*args))
       return GATTN_ERR_BUFFER_TOO_SMALL;
     return from_hip(launch_forward_gather(*args, stream));

@@ -276,4 +276,27 @@ hipError_t launch_rowwindows_fill(int32_t n, int64_t nnz, const int32_t* row_ptr
   return hipGetLastError();
 }
 
+// Per-window dispatch flag of a hybrid plan: -1 when window w goes to the MFMA
+// path (it has columns and nnz_w >= min_density * 16 * cols_w, compared in
+// double), else its edge count nnz_w (>= 0), which sizes the gather share.
+__global__ __launch_bounds__(kThreads) void hybrid_flags_kernel(int32_t n, const int32_t* __restrict__ row_ptr,
+                                                                 const int32_t* __restrict__ win_col_ptr, int32_t W,
+                                                                 float min_density, int32_t* __restrict__ flags) {
+  const int64_t w = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (w >= W) return;
+  const int32_t r0 = (int32_t)(16 * w), r1 = (int32_t)min<int64_t>(16 * w + 16, n);
+  const int32_t edges = max(row_ptr[r1] - row_ptr[r0], 0);
+  const int32_t cols = max(win_col_ptr[w + 1] - win_col_ptr[w], 0);
+  const bool dense = cols > 0 && (double)edges >= (double)min_density * 16.0 * (double)cols;
+  flags[w] = dense ? -1 : edges;
+}
+
+hipError_t launch_hybrid_flags(int32_t n, const int32_t* row_ptr, const int32_t* win_col_ptr, int32_t num_windows,
+                               float min_density, int32_t* flags, hipStream_t s) {
+  if (num_windows == 0) return hipSuccess;
+  hipLaunchKernelGGL(hybrid_flags_kernel, dim3((unsigned)ceil_div(num_windows, kThreads)), dim3(kThreads), 0, s, n,
+                     row_ptr, win_col_ptr, num_windows, min_density, flags);
+  return hipGetLastError();
+}
+
 }  // namespace gattn

@@ -134,7 +134,10 @@ uint64_t next_token() {
 }
 
 // ga carries the pointers and scalars; the geometry fields are filled here.
-hipError_t launch_gather(GatherArgs ga, const Problem& p, int part, void* ws, hipStream_t s) {
+// ranges (node partition): nullable (first row, row count) table of
+// num_ranges workgroups of at most range_rows rows.
+hipError_t launch_gather(GatherArgs ga, const Problem& p, int part, void* ws, hipStream_t s,
+                         const int32_t* ranges = nullptr, int32_t num_ranges = 0, int32_t range_rows = 0) {
   if (p.n == 0) return hipSuccess;
   const Plan g = make_plan(p);
   const Geom& ge = g.geo;
@@ -152,6 +155,12 @@ hipError_t launch_gather(GatherArgs ga, const Problem& p, int part, void* ws, hi
     ga.num_wg = (int32_t)g.B;
     ga.token = next_token();
     return detail::launch_kernels<kPartSplit>(p, ga, dim3((unsigned)g.B, (unsigned)ge.head_blocks), s);
+  }
+  if (ranges) {
+    if (num_ranges == 0) return hipSuccess;
+    ga.ranges = ranges;
+    ga.npw = range_rows;
+    return detail::launch_kernels<kPartNode>(p, ga, dim3((unsigned)num_ranges, (unsigned)ge.head_blocks), s);
   }
   ga.npw = g.npw;
   return detail::launch_kernels<kPartNode>(p, ga, dim3((unsigned)ceil_div(p.n, ga.npw), (unsigned)ge.head_blocks), s);
@@ -180,7 +189,8 @@ size_t aggregate_workspace_bytes(const gattn_aggregate_args& a) {
   return a.num_nodes == 0 ? 0 : make_plan(aggregate_problem(a)).ws_bytes;
 }
 
-hipError_t launch_forward_gather(const gattn_forward_args& a, hipStream_t s) {
+namespace {
+GatherArgs forward_gather_args(const gattn_forward_args& a) {
   GatherArgs ga = {};
   ga.row_ptr = a.row_ptr;
   ga.col_idx = a.col_idx;
@@ -198,7 +208,31 @@ hipError_t launch_forward_gather(const gattn_forward_args& a, hipStream_t s) {
   ga.eps = a.eps;
   ga.ids = a.e ? a.edge_ids : nullptr;
   ga.e_out = (uint8_t*)a.e_out;
-  return launch_gather(ga, forward_problem(a), pick_part(a.workspace), a.workspace, s);
+  return ga;
+}
+}  // namespace
+
+hipError_t launch_forward_gather(const gattn_forward_args& a, hipStream_t s) {
+  return launch_gather(forward_gather_args(a), forward_problem(a), pick_part(a.workspace), a.workspace, s);
+}
+
+int32_t gather_max_range_rows(const gattn_forward_args& a) {
+  const Problem p = forward_problem(a);
+  const Geom ge = make_geom(p, 64);
+  return std::max(1, std::min(kMaxNodesPerWg, kQLdsBytes / ge.qrow));
+}
+
+int32_t hybrid_rows_per_range(const gattn_forward_args& a, int32_t rows, int64_t nnz) {
+  Problem p = forward_problem(a);
+  p.n = std::max(rows, 1);
+  p.nnz = std::max<int64_t>(nnz, 0);
+  return make_plan(p).npw;  // at most the rows whose Q rows fit in LDS
+}
+
+hipError_t launch_forward_gather_ranges(const gattn_forward_args& a, const int32_t* ranges, int32_t num_ranges,
+                                        int32_t range_rows, hipStream_t s) {
+  return launch_gather(forward_gather_args(a), forward_problem(a), kPartNode, nullptr, s, ranges, num_ranges,
+                       range_rows);
 }
 
 hipError_t launch_aggregate_gather(const gattn_aggregate_args& a, hipStream_t s) {

@@ -42,6 +42,7 @@ struct MfmaArgs {
   const uint16_t* __restrict__ k;
   const uint16_t* __restrict__ v;
   uint16_t* __restrict__ out;
+  const int32_t* __restrict__ windows;  // nullable: the grid's windows (a hybrid plan's dense ones)
   int64_t num_cols;
   int32_t n, H, W;
   float scale_l2;  // scale * log2(e)
@@ -77,9 +78,10 @@ __global__ __launch_bounds__(kWavesPerWg * 64) void mfma_kernel(MfmaArgs a) {
   __shared__ uint16_t s_v[kWavesPerWg][16 * LDW];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int w = (int)xcd_contiguous_block(blockIdx.x, gridDim.x);
+  const int wb = (int)xcd_contiguous_block(blockIdx.x, gridDim.x);
+  const int w = a.windows ? a.windows[wb] : wb;
   const int h = blockIdx.y * kWavesPerWg + wave;
-  if (h >= a.H || w >= a.W) return;
+  if (h >= a.H || w < 0 || w >= a.W) return;
   const int r = lane & 15, g = lane >> 4;
   const int node = 16 * w + r;
   const bool row_ok = node < a.n;
@@ -216,8 +218,8 @@ __global__ __launch_bounds__(kWavesPerWg * 64) void mfma_kernel(MfmaArgs a) {
 }
 
 template <bool BF16>
-hipError_t launch_b(const gattn_forward_args& fa, const MfmaArgs& ma, hipStream_t s) {
-  dim3 grid((unsigned)ma.W, (unsigned)ceil_div(fa.num_heads, kWavesPerWg));
+hipError_t launch_b(const gattn_forward_args& fa, const MfmaArgs& ma, int32_t blocks, hipStream_t s) {
+  dim3 grid((unsigned)blocks, (unsigned)ceil_div(fa.num_heads, kWavesPerWg));
   dim3 block(kWavesPerWg * 64);
   switch (fa.head_dim) {
     case 32: hipLaunchKernelGGL((mfma_kernel<BF16, 32>), grid, block, 0, s, ma); break;
@@ -234,9 +236,11 @@ bool mfma_supported(const gattn_forward_args& a) {
          (a.head_dim == 32 || a.head_dim == 64 || a.head_dim == 128);
 }
 
-hipError_t launch_forward_mfma(const gattn_forward_args& fa, hipStream_t s) {
-  if (fa.num_nodes == 0) return hipSuccess;
+hipError_t launch_forward_mfma(const gattn_forward_args& fa, const int32_t* windows, int32_t num_windows,
+                               hipStream_t s) {
+  if (fa.num_nodes == 0 || (windows && num_windows == 0)) return hipSuccess;
   MfmaArgs ma;
+  ma.windows = windows;
   ma.win_col_ptr = fa.rw->win_col_ptr;
   ma.win_cols = fa.rw->win_cols;
   ma.tile_mask = fa.rw->tile_mask;
@@ -249,7 +253,8 @@ hipError_t launch_forward_mfma(const gattn_forward_args& fa, hipStream_t s) {
   ma.H = fa.num_heads;
   ma.W = fa.rw->num_windows;
   ma.scale_l2 = fa.scale * kLog2e;
-  return fa.dtype == GATTN_BF16 ? launch_b<true>(fa, ma, s) : launch_b<false>(fa, ma, s);
+  const int32_t blocks = windows ? num_windows : ma.W;
+  return fa.dtype == GATTN_BF16 ? launch_b<true>(fa, ma, blocks, s) : launch_b<false>(fa, ma, blocks, s);
 }
 
 }  // namespace gattn

@@ -109,6 +109,9 @@ struct GatherArgs {
   int32_t light_max;                // rows with deg + 1 <= light_max are never cut
   int32_t num_wg;                   // B: workgroups per head block
   uint64_t token;                   // this launch's flag value
+  // node partition: nullable [2 * grid] (first row, row count) of each
+  // workgroup (the gather share of a per-window hybrid plan); rows <= npw
+  const int32_t* __restrict__ ranges;
 };
 
 // First item of row r in the merged sequence (row r's edges, then its end).
@@ -291,8 +294,13 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
     const int row_end = cont_last ? __builtin_amdgcn_readfirstlane(s_cut[3]) : __builtin_amdgcn_readfirstlane(s_cut[3]) - 1;
     nn = max(0, min(row_end - n0 + 1, kMaxNodesPerWg));
   } else {
-    n0 = blk * a.npw;
-    nn = min(a.npw, a.n - n0);
+    if (a.ranges) {
+      n0 = min(max(a.ranges[2 * blk], 0), a.n);
+      nn = min(max(a.ranges[2 * blk + 1], 0), min(a.npw, a.n - n0));
+    } else {
+      n0 = blk * a.npw;
+      nn = min(a.npw, a.n - n0);
+    }
   }
   const int qcap = AGG ? 0 : kQLdsBytes / qrow;  // rows whose Q is staged in LDS
 

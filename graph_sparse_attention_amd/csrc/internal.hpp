@@ -40,7 +40,19 @@ hipError_t launch_rowwindows_fill(int32_t n, int64_t nnz, const int32_t* row_ptr
 
 // Forward -------------------------------------------------------------------
 hipError_t launch_forward_gather(const gattn_forward_args& a, hipStream_t s);
-hipError_t launch_forward_mfma(const gattn_forward_args& a, hipStream_t s);
+// windows: nullable list of the windows to run (count num_windows); else all
+hipError_t launch_forward_mfma(const gattn_forward_args& a, const int32_t* windows, int32_t num_windows, hipStream_t s);
+// gather over given (first row, row count) ranges of at most range_rows rows
+// (range_rows <= hybrid_rows_per_range for the same geometry)
+hipError_t launch_forward_gather_ranges(const gattn_forward_args& a, const int32_t* ranges, int32_t num_ranges,
+                                        int32_t range_rows, hipStream_t s);
+// most rows one gather range may hold (their Q rows must fit in LDS)
+int32_t gather_max_range_rows(const gattn_forward_args& a);
+// rows per gather range of a hybrid plan whose gather share has `rows` rows and `nnz` edges
+int32_t hybrid_rows_per_range(const gattn_forward_args& a, int32_t rows, int64_t nnz);
+// flags[w] = -1 when window w goes to the MFMA path, else its edge count (see gattn_build_hybrid)
+hipError_t launch_hybrid_flags(int32_t n, const int32_t* row_ptr, const int32_t* win_col_ptr, int32_t num_windows,
+                               float min_density, int32_t* flags, hipStream_t s);
 hipError_t launch_aggregate_gather(const gattn_aggregate_args& a, hipStream_t s);
 // bytes of the workspace that selects the balanced partition (0 for N = 0)
 size_t forward_gather_workspace_bytes(const gattn_forward_args& a);

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GATTN_ABI_VERSION 3
+#define GATTN_ABI_VERSION 4
 
 #ifndef GATTN_API
 #define GATTN_API __attribute__((visibility("default")))
@@ -83,7 +83,12 @@ typedef enum {
   GATTN_SOFTMAX_CLIPPED = 1
 } gattn_mode;
 
-typedef enum { GATTN_PATH_AUTO = 0, GATTN_PATH_GATHER = 1, GATTN_PATH_MFMA = 2 } gattn_path;
+typedef enum {
+  GATTN_PATH_AUTO = 0,
+  GATTN_PATH_GATHER = 1,
+  GATTN_PATH_MFMA = 2,
+  GATTN_PATH_HYBRID = 3  /* per row window: dense windows on the MFMA path, the rest gathered */
+} gattn_path;
 
 #define GATTN_FLAG_VALIDATE 1u /* gattn_forward: copy row_ptr / col_idx to the host and check them
                                   first (a debugging aid; synchronizes the stream)              */
@@ -155,6 +160,17 @@ typedef struct {
   const uint16_t* tile_mask;   /* [num_cols] = [num_cols/16][16]               */
 } gattn_rowwindows;
 
+/* Per-window dispatch plan (from gattn_build_hybrid): which row windows run
+ * on the MFMA path and which destination ranges the gather path takes.  The
+ * windows and ranges together cover every row exactly once.                */
+typedef struct {
+  int32_t num_dense;             /* windows on the MFMA path                            */
+  int32_t num_ranges;            /* gather workgroups                                   */
+  int32_t range_rows;            /* most rows in one range                              */
+  const int32_t* dense_windows;  /* [num_dense] ascending window ids (device)           */
+  const int32_t* ranges;         /* [2 * num_ranges] (first row, row count) (device)    */
+} gattn_hybrid;
+
 typedef struct {
   uint32_t struct_size;        /* sizeof(gattn_forward_args)                         */
   int32_t num_nodes;           /* N >= 0                                             */
@@ -173,8 +189,10 @@ typedef struct {
   float scale;                 /* > 0; usually 1/sqrt(D)                             */
   float clip_lo, clip_hi;      /* clipped mode (RTMScore: -5, 5)                     */
   float eps;                   /* clipped mode denominator term, >= 0                */
-  gattn_path path;             /* AUTO picks MFMA when it applies and rw is given    */
-  const gattn_rowwindows* rw;  /* [host] struct of device arrays; MFMA path only     */
+  gattn_path path;             /* AUTO: HYBRID when `hybrid` is given and the MFMA
+                                  path applies, else MFMA when rw is given and dense
+                                  enough, else GATHER                                  */
+  const gattn_rowwindows* rw;  /* [host] struct of device arrays; MFMA / HYBRID paths */
   uint32_t flags;              /* GATTN_FLAG_*                                       */
   /* Edge-id indirection (the article's map from CSC position to edge id):
      nullable [nnz] int32; when set, the per-edge rows of e and e_out are
@@ -201,6 +219,10 @@ typedef struct {
      run at the same time.  Ignored on the MFMA path.                           */
   void* workspace;
   size_t workspace_bytes;
+  /* Per-window plan for the HYBRID path: [host] struct of device arrays built
+     by gattn_build_hybrid for this graph, these row windows and this geometry
+     (H, D, dtype, mode, e).  Nullable; required by GATTN_PATH_HYBRID.          */
+  const gattn_hybrid* hybrid;
 } gattn_forward_args;
 
 /* out[i, h, :] = sum_p alpha_p(h) v[col_idx[p], h, :] over the in-edges p of i;
@@ -212,6 +234,32 @@ GATTN_API gattn_status gattn_forward(const gattn_forward_args* args /*[host]*/, 
 
 /* The path gattn_forward would take for these arguments (no work enqueued; `out` may be NULL). */
 GATTN_API gattn_status gattn_forward_path(const gattn_forward_args* args /*[host]*/, gattn_path* path /*[host]*/);
+
+/* ------------------------------------------------------------------------
+ * gattn_build_hybrid: per-window dispatch between the MFMA row-window path and
+ * the gather path.  Fused3S (Figure 1) compacts every row window into dense
+ * tensor-core blocks; a window whose blocks are mostly empty wastes the
+ * matrix-core work and reloads K / V rows for few edges, so this plan keeps
+ * the row windows only where they are dense (the per-window choice is this
+ * library's, not the page's).  Window w (rows 16w .. 16w+15) goes to the MFMA path when it
+ * has columns and its tile density nnz_w / (16 * cols_w) >= min_density
+ * (nnz_w = edges of its rows, cols_w = win_col_ptr[w+1] - win_col_ptr[w]);
+ * the rows of the other windows are cut into gather ranges of consecutive
+ * rows, sized like the gather path's workgroups for the sparse part.
+ *   args: the forward arguments the plan is for (graph, sizes, dtype, mode,
+ *         e, rw); `out`, `hybrid` and the tensors' contents are not read.
+ *         The MFMA path must apply (fp16 / bf16, standard mode, no e).
+ *   min_density in [0, 1]; 0 sends every window with columns to the MFMA
+ *         path, a value above 1 sends every window to the gather path.
+ *   dense_windows: device int32 [ceil(N/16)] out; ranges: device int32 [2N]
+ *         out (capacities that hold any plan).
+ *   plan: [host] out; its pointers are dense_windows and ranges.
+ * Synchronizes `stream` (the lists are built on the host from one flag per
+ * window); a once-per-graph preprocessing step like the row windows.
+ * ------------------------------------------------------------------------ */
+GATTN_API gattn_status gattn_build_hybrid(const gattn_forward_args* args /*[host]*/, float min_density,
+                                          int32_t* dense_windows, int32_t* ranges, gattn_hybrid* plan /*[host]*/,
+                                          hipStream_t stream);
 
 /* Workspace bytes for the balanced gather partition of these arguments (sizes,
  * dtype, mode, whether e and e_out are given; pointers are not read).  0 when

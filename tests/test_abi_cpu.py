@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(gsa):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     lib = ctypes.CDLL(gsa.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), f"{name} declared in gattn.h but not exported"
@@ -46,10 +46,11 @@ def test_enums_and_strings(gsa):
                  "GATTN_ERR_DUPLICATE_EDGE", "GATTN_ERR_BUFFER_TOO_SMALL", "GATTN_ERR_HIP"]:
         m = re.search(name + r"\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(gsa, name)
-    assert gsa.gattn_abi_version() == 3
+    assert gsa.gattn_abi_version() == 4
     assert gsa.gattn_status_string(gsa.GATTN_ERR_DUPLICATE_EDGE).startswith("repeated")
     assert gsa.gattn_status_string(99) == "unknown status"
-    assert ctypes.sizeof(gsa._ForwardArgs) == 160
+    assert ctypes.sizeof(gsa._ForwardArgs) == 168
+    assert ctypes.sizeof(gsa._Hybrid) == 32
     assert ctypes.sizeof(gsa._AggregateArgs) == 104
 
 
@@ -133,6 +134,68 @@ def test_path_resolution(gsa):
     assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_GATHER)           # inconsistent windows ignored
     a.path = gsa.GATTN_PATH_MFMA
     assert path_of(gsa, a)[0] == gsa.GATTN_ERR_INVALID_VALUE
+
+
+def fake_hybrid(gsa, **kw):
+    base = 1 << 32
+    h = gsa._Hybrid(3, 4, 8, base + (30 << 20), base + (31 << 20))   # this geometry stages 12 Q rows
+    for k, v in kw.items():
+        setattr(h, k, v)
+    return h
+
+
+def test_hybrid_path_checks(gsa):
+    L = gsa._lib
+    base = 1 << 32
+    rw = gsa._RowWindows(7, 16 * 10, base + (10 << 20), base + (11 << 20), base + (12 << 20))
+    hy = fake_hybrid(gsa)
+    # the hybrid path needs the MFMA path's conditions, row windows and a plan
+    a = fake_args(gsa, path=gsa.GATTN_PATH_HYBRID)
+    assert path_of(gsa, a)[0] == gsa.GATTN_ERR_INVALID_VALUE                  # no row windows
+    a.rw = ctypes.pointer(rw)
+    assert path_of(gsa, a)[0] == gsa.GATTN_ERR_INVALID_VALUE                  # no plan
+    a.hybrid = ctypes.pointer(hy)
+    assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_HYBRID)
+    for kw in (dict(num_dense=8), dict(num_dense=-1), dict(num_ranges=101), dict(range_rows=0),
+               dict(range_rows=100000), dict(dense_windows=None), dict(ranges=None), dict(ranges=base + 2)):
+        bad = fake_hybrid(gsa, **kw)
+        a.hybrid = ctypes.pointer(bad)
+        assert path_of(gsa, a)[0] == gsa.GATTN_ERR_INVALID_VALUE, kw
+        assert L.gattn_forward(ctypes.byref(a), None) == gsa.GATTN_ERR_INVALID_VALUE, kw
+    a.hybrid = ctypes.pointer(hy)
+    a.dtype = gsa.GATTN_F32
+    assert path_of(gsa, a)[0] == gsa.GATTN_ERR_UNSUPPORTED
+    # AUTO takes a plan when the MFMA path applies, and ignores it otherwise
+    a = fake_args(gsa, rw=ctypes.pointer(rw), hybrid=ctypes.pointer(hy))
+    assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_HYBRID)
+    a.e = base + (14 << 20)
+    assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_GATHER)
+
+
+def test_build_hybrid_argument_errors(gsa):
+    L = gsa._lib
+    base = 1 << 32
+    rw = gsa._RowWindows(7, 16 * 10, base + (10 << 20), base + (11 << 20), base + (12 << 20))
+    plan = gsa._Hybrid()
+    dw, rg = ctypes.c_void_p(base + (30 << 20)), ctypes.c_void_p(base + (31 << 20))
+    a = fake_args(gsa, rw=ctypes.pointer(rw))
+    assert L.gattn_build_hybrid(ctypes.byref(a), 0.25, dw, rg, None, None) == gsa.GATTN_ERR_INVALID_VALUE
+    for d in (-0.5, float("nan"), float("inf")):
+        assert L.gattn_build_hybrid(ctypes.byref(a), d, dw, rg, ctypes.byref(plan), None) == gsa.GATTN_ERR_INVALID_VALUE
+    assert L.gattn_build_hybrid(ctypes.byref(a), 0.25, None, rg, ctypes.byref(plan), None) == gsa.GATTN_ERR_INVALID_VALUE
+    assert L.gattn_build_hybrid(ctypes.byref(a), 0.25, dw, ctypes.c_void_p(base + 2), ctypes.byref(plan),
+                                None) == gsa.GATTN_ERR_INVALID_VALUE
+    b = fake_args(gsa)                                                        # no row windows
+    assert L.gattn_build_hybrid(ctypes.byref(b), 0.25, dw, rg, ctypes.byref(plan), None) == gsa.GATTN_ERR_INVALID_VALUE
+    b = fake_args(gsa, rw=ctypes.pointer(rw), dtype=gsa.GATTN_F32)            # no MFMA path for fp32
+    assert L.gattn_build_hybrid(ctypes.byref(b), 0.25, dw, rg, ctypes.byref(plan), None) == gsa.GATTN_ERR_UNSUPPORTED
+    b = fake_args(gsa, rw=ctypes.pointer(rw), mode=gsa.GATTN_SOFTMAX_CLIPPED)
+    assert L.gattn_build_hybrid(ctypes.byref(b), 0.25, dw, rg, ctypes.byref(plan), None) == gsa.GATTN_ERR_UNSUPPORTED
+    # an empty graph: an empty plan, no HIP call
+    rw0 = gsa._RowWindows(0, 0, base + (10 << 20), None, None)
+    z = fake_args(gsa, num_nodes=0, nnz=0, rw=ctypes.pointer(rw0))
+    assert L.gattn_build_hybrid(ctypes.byref(z), 0.25, None, None, ctypes.byref(plan), None) == gsa.GATTN_OK
+    assert (plan.num_dense, plan.num_ranges) == (0, 0)
 
 
 def test_build_argument_errors(gsa):

@@ -302,7 +302,33 @@ def gen_config5(seed=0, num_graphs=1024) -> Workload:
                     8, 64, "f16", "standard", False, seed=seed)
 
 
-GENERATORS = {1: gen_config1, 2: gen_config2, 3: gen_config3, 4: gen_config4, 5: gen_config5}
+def gen_mixed(seed=0, num_pairs=512) -> Workload:
+    """Mixed-density batch for the per-window hybrid dispatch (not one of the
+    five benchmark configurations): num_pairs pairs of a complete digraph with
+    self loops (n ~ U{20..40}, dense row windows) followed by a sparse block
+    (n ~ U{100..300}, in-degree ~ Poisson(4) capped at n, distinct sources
+    uniform inside the block); block-diagonal numbering."""
+    g = rng_for(6, STREAM_GRAPH, seed)
+    srcs, dsts = [], []
+    off = 0
+    for _ in range(num_pairs):
+        n = int(g.integers(20, 41))
+        a = np.arange(n) + off
+        srcs.append(np.tile(a, n))
+        dsts.append(np.repeat(a, n))
+        off += n
+        m = int(g.integers(100, 301))
+        deg = np.minimum(g.poisson(4.0, size=m), m)
+        s, d = _distinct_uniform_sources(g, deg, m)
+        srcs.append(s + off)
+        dsts.append(d + off)
+        off += m
+    src, dst = _order_by_source(np.concatenate(srcs), np.concatenate(dsts), off)
+    return Workload(6, f"mixed batch {num_pairs} complete digraphs + {num_pairs} sparse blocks H=8 D=64 fp16 standard",
+                    off, src, dst, 8, 64, "f16", "standard", False, seed=seed)
+
+
+GENERATORS = {1: gen_config1, 2: gen_config2, 3: gen_config3, 4: gen_config4, 5: gen_config5, 6: gen_mixed}
 
 
 def make(config: int, seed: int = 0, **kw) -> Workload:
