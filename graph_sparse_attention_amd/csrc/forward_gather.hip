@@ -84,7 +84,7 @@ Plan make_plan(const Problem& p) {
   Plan g{};
   g.geo = make_geom(p, 64);
   if (p.n == 0) return g;
-  const int u = p.he ? GATTN_GATHER_U_E : GATTN_GATHER_U;
+  const int u = detail::unroll_of(p);
   const int cus = device_cus();
   auto qcap_of = [&](const Geom& ge) {
     return p.mode == kModeAggregate ? kMaxNodesPerWg : std::max(1, std::min(kMaxNodesPerWg, kQLdsBytes / ge.qrow));
@@ -166,14 +166,17 @@ hipError_t launch_gather(GatherArgs ga, const Problem& p, int part, void* ws, hi
   return detail::launch_kernels<kPartNode>(p, ga, dim3((unsigned)ceil_div(p.n, ga.npw), (unsigned)ge.head_blocks), s);
 }
 
+bool low_degree(int32_t n, int64_t nnz) { return n > 0 && (double)nnz < GATTN_GATHER_LOW_DEGREE * (double)n; }
+
 Problem forward_problem(const gattn_forward_args& a) {
   const bool he = a.e != nullptr;
   return Problem{a.num_nodes, a.num_heads, a.head_dim, a.nnz, a.dtype, a.mode, he,
-                 a.e_out != nullptr && he && a.mode == GATTN_SOFTMAX_CLIPPED};
+                 a.e_out != nullptr && he && a.mode == GATTN_SOFTMAX_CLIPPED, low_degree(a.num_nodes, a.nnz)};
 }
 
 Problem aggregate_problem(const gattn_aggregate_args& a) {
-  return Problem{a.num_nodes, a.num_heads, a.head_dim, a.nnz, a.dtype, kModeAggregate, false, false};
+  return Problem{a.num_nodes, a.num_heads, a.head_dim, a.nnz, a.dtype, kModeAggregate, false, false,
+                 low_degree(a.num_nodes, a.nnz)};
 }
 
 // A workspace selects the balanced partition.

@@ -60,6 +60,12 @@
 #ifndef GATTN_GATHER_U
 #define GATTN_GATHER_U 8                // edges per step without an edge tensor
 #endif
+#ifndef GATTN_GATHER_U_LOW
+#define GATTN_GATHER_U_LOW 4            // the same for graphs of low average degree
+#endif
+#ifndef GATTN_GATHER_LOW_DEGREE
+#define GATTN_GATHER_LOW_DEGREE 8.0     // average in-degree below which U_LOW is used
+#endif
 #ifndef GATTN_GATHER_U_E
 #define GATTN_GATHER_U_E 4              // edges per step with an edge tensor
 #endif
@@ -628,42 +634,55 @@ struct Problem {
   gattn_dtype dtype;
   int mode;
   bool he, eout;
+  bool low;  // low average degree: fewer edges per step (standard without E, aggregate)
 };
 
 
 namespace detail {
 
-template <int MODE, bool HAS_E>
-constexpr int unroll() { return HAS_E ? GATTN_GATHER_U_E : GATTN_GATHER_U; }
+// Edges per step: U_E with an edge tensor, else U, or U_LOW for graphs of
+// low average degree (standard mode and aggregation): with few edges per
+// destination a shorter step keeps fewer registers and more waves resident.
+inline int unroll_of(const Problem& p) {
+  if (p.he) return GATTN_GATHER_U_E;
+  return p.low && p.mode != GATTN_SOFTMAX_CLIPPED ? GATTN_GATHER_U_LOW : GATTN_GATHER_U;
+}
 
-template <typename T, int D, int MODE, bool HAS_E, bool EOUT, int PART>
-constexpr auto kernel_of() { return gather_kernel<T, D, MODE, HAS_E, EOUT, unroll<MODE, HAS_E>(), PART>; }
+template <typename T, int D, int MODE, bool HAS_E, bool EOUT, int PART, int U>
+constexpr auto kernel_of() { return gather_kernel<T, D, MODE, HAS_E, EOUT, U, PART>; }
 
 // Workgroups of one instantiation that fit on a CU at once (queried once).
-template <typename T, int D, int MODE, bool HAS_E, bool EOUT, int PART>
+template <typename T, int D, int MODE, bool HAS_E, bool EOUT, int PART, int U>
 int resident_per_cu() {
   static const int per_cu = [] {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kernel_of<T, D, MODE, HAS_E, EOUT, PART>(), kGatherThreads,
-                                                     0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kernel_of<T, D, MODE, HAS_E, EOUT, PART, U>(),
+                                                     kGatherThreads, 0) != hipSuccess)
       b = 1;
     return std::max(b, 1);
   }();
   return per_cu;
 }
 
-// Calls F::template run<T, D, MODE, HAS_E, EOUT>() for the instantiation of p.
-// The instantiations that exist: standard +-E, clipped +-E (+ edge update
-// with E), aggregate.
+// Calls F::template run<T, D, MODE, HAS_E, EOUT, U>() for the instantiation
+// of p.  The instantiations that exist: standard +-E, clipped +-E (+ edge
+// update with E), aggregate; the standard mode without E and the aggregate
+// also with the low-degree step.
 template <typename F, typename T, int D>
 auto by_variant(const Problem& p, const F& f) {
-  if (p.mode == kModeAggregate) return f.template run<T, D, kModeAggregate, false, false>();
-  if (p.mode == GATTN_SOFTMAX_STANDARD)
-    return p.he ? f.template run<T, D, GATTN_SOFTMAX_STANDARD, true, false>()
-                : f.template run<T, D, GATTN_SOFTMAX_STANDARD, false, false>();
-  if (!p.he) return f.template run<T, D, GATTN_SOFTMAX_CLIPPED, false, false>();
-  return p.eout ? f.template run<T, D, GATTN_SOFTMAX_CLIPPED, true, true>()
-                : f.template run<T, D, GATTN_SOFTMAX_CLIPPED, true, false>();
+  constexpr int UE = GATTN_GATHER_U_E, UN = GATTN_GATHER_U, UL = GATTN_GATHER_U_LOW;
+  const bool low = unroll_of(p) == UL && UL != UN;
+  if (p.mode == kModeAggregate)
+    return low ? f.template run<T, D, kModeAggregate, false, false, UL>()
+               : f.template run<T, D, kModeAggregate, false, false, UN>();
+  if (p.mode == GATTN_SOFTMAX_STANDARD) {
+    if (p.he) return f.template run<T, D, GATTN_SOFTMAX_STANDARD, true, false, UE>();
+    return low ? f.template run<T, D, GATTN_SOFTMAX_STANDARD, false, false, UL>()
+               : f.template run<T, D, GATTN_SOFTMAX_STANDARD, false, false, UN>();
+  }
+  if (!p.he) return f.template run<T, D, GATTN_SOFTMAX_CLIPPED, false, false, UN>();
+  return p.eout ? f.template run<T, D, GATTN_SOFTMAX_CLIPPED, true, true, UE>()
+                : f.template run<T, D, GATTN_SOFTMAX_CLIPPED, true, false, UE>();
 }
 
 template <typename F, typename T>
@@ -687,8 +706,8 @@ auto dispatch(const Problem& p, const F& f) {
 
 template <int PART>
 struct Resident {
-  template <typename T, int D, int MODE, bool HAS_E, bool EOUT>
-  int run() const { return resident_per_cu<T, D, MODE, HAS_E, EOUT, PART>(); }
+  template <typename T, int D, int MODE, bool HAS_E, bool EOUT, int U>
+  int run() const { return resident_per_cu<T, D, MODE, HAS_E, EOUT, PART, U>(); }
 };
 
 template <int PART>
@@ -696,9 +715,9 @@ struct Launch {
   const GatherArgs& ga;
   dim3 grid;
   hipStream_t s;
-  template <typename T, int D, int MODE, bool HAS_E, bool EOUT>
+  template <typename T, int D, int MODE, bool HAS_E, bool EOUT, int U>
   hipError_t run() const {
-    hipLaunchKernelGGL((kernel_of<T, D, MODE, HAS_E, EOUT, PART>()), grid, dim3(kGatherThreads), 0, s, ga);
+    hipLaunchKernelGGL((kernel_of<T, D, MODE, HAS_E, EOUT, PART, U>()), grid, dim3(kGatherThreads), 0, s, ga);
     return hipGetLastError();
   }
 };
