@@ -25,11 +25,15 @@
 //    one block of heads.  It first stages the destinations' row pointers and
 //    Q rows in LDS (one coalesced pass).  Its edges are then cut into NS equal
 //    contiguous pieces (a merge path over the CSR): each slot walks its piece
-//    U edges at a time, prefetching the next piece of column indices (and E
-//    rows) while it computes, and keeps the online-softmax state (m, l) and
-//    the fp32 accumulator in registers.  A destination that is cut by a piece
-//    boundary leaves partial (m, l, acc) records in LDS; the slot holding its
-//    last edge merges them in slot order.  Deterministic, no atomics.
+//    U edges at a time (U = 4 with an edge tensor or a low average degree,
+//    else 8), loading the next step's column indices and E rows (edge ids two
+//    steps ahead) while it computes, and keeps the online-softmax state
+//    (m, l) and the fp32 accumulator in registers.  A destination that is cut
+//    by a piece boundary leaves partial (m, l, acc) records in LDS; the slot
+//    holding its last edge merges them in slot order.  Deterministic, no
+//    atomics.  The destination range is either equal-sized (node partition)
+//    or read from a table of (first row, row count) pairs (the gather share
+//    of a per-window hybrid plan).
 //  * Consecutive workgroups are mapped onto one XCD so that destinations of
 //    one batched graph, whose sources are nearby, share an L2.
 //  * With a workspace, workgroups instead take equal ranges of the merged
