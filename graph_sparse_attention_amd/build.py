@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libgattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "scan.hip", "build_csr.hip", "build_rowwindows.hip", "forward_gather.hip",
+SOURCES = ["api.cpp", "scan.hip", "build_csr.hip", "build_csr_radix.hip", "build_rowwindows.hip", "forward_gather.hip",
            "forward_gather_split.hip", "forward_mfma.hip"]
 
 COMMON = ["-O3", "-fPIC", "-fvisibility=hidden", "-std=c++17", "-Wall", "-Wno-unused-function", f"--offload-arch={ARCH}",

@@ -7,7 +7,8 @@
 // fix the order inside a destination; we sort it by (source, edge id), which
 // makes the result unique although the scatter below uses atomics.
 //
-// Five launches: clear the scratch -> count in-degrees (atomics) and flag bad
+// Counting build (edge lists below 2^18; build_csr_radix.hip serves the
+// larger ones with the same result).  Five launches: clear the scratch -> count in-degrees (atomics) and flag bad
 // indices -> single-pass exclusive scan -> scatter 64-bit keys (src << 32 |
 // edge id), each destination counting its in-degree back down for positions
 // -> sort every destination's keys (bitonic across the lanes of one wave, four
@@ -16,11 +17,15 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <stdlib.h>
+#include <string.h>
+
 namespace gattn {
 
 namespace {
 
 constexpr int kRowCap = 2048;  // keys per LDS sort (16 KiB)
+constexpr int64_t kRadixMinEdges = 1 << 18;
 
 // flag words at the head of the workspace
 enum { kBad = 0, kScanErr = 2, kTicket = 3 };
@@ -125,106 +130,145 @@ __device__ void lds_bitonic(uint64_t* s, int P) {
   }
 }
 
-// A workgroup sorts 16 destinations.  Each wave takes four: side by side in
+// A workgroup sorts groups of 16 destinations (grid-stride).  Each wave takes four: side by side in
 // 16-lane segments when all have <= 16 in-edges, else one after the other
 // across the wave (<= 64).  Longer rows are listed in LDS and sorted by the
 // whole workgroup afterwards: in LDS up to kRowCap keys, beyond that as
 // LDS-sorted chunks written back and ranked against each other.
-__global__ __launch_bounds__(256) void sort_rows_kernel(int32_t n, const int32_t* __restrict__ row_ptr,
+// a row's [start, start + degree) clamped to [0, nnz): a damaged row_ptr cannot
+// send a read or write outside the key and output arrays
+__device__ __forceinline__ void row_range(const int32_t* row_ptr, int64_t r, int32_t nnz, int32_t& st, int32_t& d) {
+  const int32_t a = min(max(row_ptr[r], 0), nnz);
+  const int32_t b = min(max(row_ptr[r + 1], a), nnz);
+  st = a;
+  d = b - a;
+}
+
+__global__ __launch_bounds__(256) void sort_rows_kernel(int32_t n, int32_t nnz, const int32_t* __restrict__ row_ptr,
                                                         uint64_t* __restrict__ keys, int32_t* __restrict__ col_idx,
-                                                        int32_t* __restrict__ edge_perm) {
+                                                        int32_t* __restrict__ edge_perm,
+                                                        const int32_t* __restrict__ run_flag) {
+  if (run_flag && *run_flag == 0) return;  // rows already in order (radix build, sorted sources)
   __shared__ uint64_t s[kRowCap];
   __shared__ int32_t s_long[16];
   __shared__ int32_t s_nlong;
   const int lane = threadIdx.x & 63;
-  if (threadIdx.x == 0) s_nlong = 0;
-  __syncthreads();
-  const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4;
-  if (r0 < n) {
-    const int nr = (int)min<int64_t>(4, n - r0);
-    int st[4], d[4], dmax = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      st[i] = i < nr ? row_ptr[r0 + i] : 0;
-      d[i] = i < nr ? row_ptr[r0 + i + 1] - st[i] : 0;
-      dmax = max(dmax, d[i]);
-    }
-    if (dmax <= 16) {
-      const int i = lane >> 4, t = lane & 15;
-      const int64_t p = (int64_t)st[i] + t;
-      uint64_t key = t < d[i] ? keys[p] : ~0ull;
-      key = lane_bitonic(key, lane, 16);
-      if (t < d[i]) emit(col_idx, edge_perm, p, key);
-    } else {
+  const int64_t groups = (n + 15) / 16;
+  for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+    if (threadIdx.x == 0) s_nlong = 0;
+    __syncthreads();
+    const int64_t r0 = (grp * 4 + (threadIdx.x >> 6)) * 4;
+    if (r0 < n) {
+      const int nr = (int)min<int64_t>(4, n - r0);
+      int st[4], d[4], dmax = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (d[i] <= 1) {
-          if (d[i] == 1 && lane == 0) emit(col_idx, edge_perm, st[i], keys[st[i]]);
-          continue;
-        }
-        if (d[i] > 64) {
-          if (lane == 0) s_long[atomicAdd(&s_nlong, 1)] = (int32_t)(r0 + i);
-          continue;
-        }
-        int P = 2;
-        while (P < d[i]) P <<= 1;
-        uint64_t key = lane < d[i] ? keys[st[i] + lane] : ~0ull;
-        key = lane_bitonic(key, lane, P);
-        if (lane < d[i]) emit(col_idx, edge_perm, st[i] + lane, key);
+        st[i] = 0;
+        d[i] = 0;
+        if (i < nr) row_range(row_ptr, r0 + i, nnz, st[i], d[i]);
+        dmax = max(dmax, d[i]);
       }
-    }
-  }
-  __syncthreads();
-  const int nlong = s_nlong;
-  for (int li = 0; li < nlong; ++li) {
-    const int32_t r = s_long[li];
-    const int32_t st = row_ptr[r], d = row_ptr[r + 1] - st;
-    const int nchunks = (d + kRowCap - 1) / kRowCap;
-    for (int c = 0; c < nchunks; ++c) {
-      const int cs = c * kRowCap, cl = min(kRowCap, d - cs);
-      int P = 1;
-      while (P < cl) P <<= 1;
-      for (int i = threadIdx.x; i < P; i += blockDim.x) s[i] = i < cl ? keys[st + cs + i] : ~0ull;
-      __syncthreads();
-      lds_bitonic(s, P);
-      if (nchunks == 1) {
-        for (int i = threadIdx.x; i < cl; i += blockDim.x) emit(col_idx, edge_perm, st + i, s[i]);
+      if (dmax <= 16) {
+        const int i = lane >> 4, t = lane & 15;
+        const int64_t p = (int64_t)st[i] + t;
+        uint64_t key = t < d[i] ? keys[p] : ~0ull;
+        key = lane_bitonic(key, lane, 16);
+        if (t < d[i]) emit(col_idx, edge_perm, p, key);
       } else {
-        for (int i = threadIdx.x; i < cl; i += blockDim.x) keys[st + cs + i] = s[i];
-      }
-      __syncthreads();
-    }
-    if (nchunks > 1) {
-      // rank of a key = its index in its own sorted chunk + keys below it in the others
-      for (int i = threadIdx.x; i < d; i += blockDim.x) {
-        const uint64_t key = keys[st + i];
-        const int own = i / kRowCap;
-        int rank = i - own * kRowCap;
-        for (int c = 0; c < nchunks; ++c) {
-          if (c == own) continue;
-          int lo = c * kRowCap, hi = min(lo + kRowCap, d);
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (keys[st + mid] < key) lo = mid + 1; else hi = mid;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (d[i] <= 1) {
+            if (d[i] == 1 && lane == 0) emit(col_idx, edge_perm, st[i], keys[st[i]]);
+            continue;
           }
-          rank += lo - c * kRowCap;
+          if (d[i] > 64) {
+            if (lane == 0) s_long[atomicAdd(&s_nlong, 1)] = (int32_t)(r0 + i);
+            continue;
+          }
+          int P = 2;
+          while (P < d[i]) P <<= 1;
+          uint64_t key = lane < d[i] ? keys[st[i] + lane] : ~0ull;
+          key = lane_bitonic(key, lane, P);
+          if (lane < d[i]) emit(col_idx, edge_perm, st[i] + lane, key);
         }
-        emit(col_idx, edge_perm, st + rank, key);
       }
-      __syncthreads();
     }
+    __syncthreads();
+    const int nlong = s_nlong;
+    for (int li = 0; li < nlong; ++li) {
+      const int32_t r = s_long[li];
+      int32_t st, d;
+      row_range(row_ptr, r, nnz, st, d);
+      const int nchunks = (d + kRowCap - 1) / kRowCap;
+      for (int c = 0; c < nchunks; ++c) {
+        const int cs = c * kRowCap, cl = min(kRowCap, d - cs);
+        int P = 1;
+        while (P < cl) P <<= 1;
+        for (int i = threadIdx.x; i < P; i += blockDim.x) s[i] = i < cl ? keys[st + cs + i] : ~0ull;
+        __syncthreads();
+        lds_bitonic(s, P);
+        if (nchunks == 1) {
+          for (int i = threadIdx.x; i < cl; i += blockDim.x) emit(col_idx, edge_perm, st + i, s[i]);
+        } else {
+          for (int i = threadIdx.x; i < cl; i += blockDim.x) keys[st + cs + i] = s[i];
+        }
+        __syncthreads();
+      }
+      if (nchunks > 1) {
+        // rank of a key = its index in its own sorted chunk + keys below it in the others
+        for (int i = threadIdx.x; i < d; i += blockDim.x) {
+          const uint64_t key = keys[st + i];
+          const int own = i / kRowCap;
+          int rank = i - own * kRowCap;
+          for (int c = 0; c < nchunks; ++c) {
+            if (c == own) continue;
+            int lo = c * kRowCap, hi = min(lo + kRowCap, d);
+            while (lo < hi) {
+              const int mid = (lo + hi) >> 1;
+              if (keys[st + mid] < key) lo = mid + 1; else hi = mid;
+            }
+            rank += lo - c * kRowCap;
+          }
+          emit(col_idx, edge_perm, st + rank, key);
+        }
+        __syncthreads();
+      }
+    }
+    __syncthreads();  // s_long / s_nlong are reused by the next group
   }
 }
 
 }  // namespace
 
+hipError_t launch_sort_rows(int32_t n, int64_t nnz, const int32_t* row_ptr, uint64_t* keys, int32_t* col_idx, int32_t* edge_perm,
+                            const int32_t* run_flag, hipStream_t s) {
+  if (n > 0)
+    hipLaunchKernelGGL(sort_rows_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(n, 16), 8192)), dim3(256), 0, s, n, (int32_t)nnz, row_ptr, keys,
+                       col_idx, edge_perm, run_flag);
+  return hipGetLastError();
+}
+
+// The counting build serves small edge lists, the radix build large ones;
+// GATTN_CSR_PATH=atomic|radix in the environment overrides the choice.
+bool csr_use_radix(int32_t n, int64_t nnz) {
+  if (n < 1 || nnz < 1) return false;
+  if (const char* e = getenv("GATTN_CSR_PATH")) {
+    if (!strcmp(e, "radix")) return true;
+    if (!strcmp(e, "atomic")) return false;
+  }
+  return nnz >= kRadixMinEdges;
+}
+
 size_t build_csr_workspace_bytes(int32_t n, int64_t nnz) {
+  if (csr_use_radix(n, nnz)) return build_csr_radix_workspace_bytes(n, nnz);
   return 256 + align256(sizeof(int32_t) * std::max<int64_t>(n, 1)) + align256(sizeof(uint64_t) * scan_tiles(n)) +
          align256(sizeof(uint64_t) * std::max<int64_t>(nnz, 1));
 }
 
 hipError_t launch_build_csr(int32_t n, int64_t nnz, const int32_t* src, const int32_t* dst, int32_t* row_ptr,
                             int32_t* col_idx, int32_t* edge_perm, void* ws, int32_t* status_dev, hipStream_t s) {
+  if (csr_use_radix(n, nnz))
+    return launch_build_csr_radix(n, nnz, src, dst, row_ptr, col_idx, edge_perm, ws, status_dev, s);
   CsrWs w = carve(ws, n, nnz);
   const unsigned cblocks = (unsigned)std::min<int64_t>(ceil_div(w.clear_ints, 256), 2048);
   hipLaunchKernelGGL(init_kernel, dim3(cblocks), dim3(256), 0, s, w.flags, w.clear_ints, status_dev);
@@ -236,8 +280,7 @@ hipError_t launch_build_csr(int32_t n, int64_t nnz, const int32_t* src, const in
   if (err != hipSuccess) return err;
   if (nnz > 0 && n > 0) {
     hipLaunchKernelGGL(scatter_kernel, dim3(eblocks), dim3(256), 0, s, src, dst, nnz, n, row_ptr, w.counts, w.keys);
-    hipLaunchKernelGGL(sort_rows_kernel, dim3((unsigned)ceil_div(n, 16)), dim3(256), 0, s, n, row_ptr, w.keys, col_idx,
-                       edge_perm);
+    return launch_sort_rows(n, nnz, row_ptr, w.keys, col_idx, edge_perm, nullptr, s);
   }
   return hipGetLastError();
 }

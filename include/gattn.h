@@ -108,7 +108,11 @@ GATTN_API const char* gattn_status_string(gattn_status s);
  *   edge_perm   [nnz] int32 out, nullable: edge id of each CSR position (use it
  *               to bring per-edge tensors such as E into CSR order).
  *   workspace   device scratch of at least gattn_build_csr_workspace() bytes,
- *               256-byte aligned.
+ *               256-byte aligned (about 8 bytes per edge below 2^18 edges, 25
+ *               above, where a radix sort replaces per-edge atomics; the two
+ *               builds give the same bits; GATTN_CSR_PATH=atomic|radix in the
+ *               environment forces one of them, for tests and measurement, and
+ *               must not change between the size query and the call).
  *   status_dev  nullable device int32.  NULL: the call synchronizes `stream` and
  *               returns GATTN_ERR_BAD_GRAPH when any src/dst lies outside
  *               [0, num_nodes).  Non-NULL: the call stays asynchronous and the

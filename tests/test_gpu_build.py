@@ -35,17 +35,66 @@ def assert_csr_equal(gsa, n, src, dst):
     return ref
 
 
+@pytest.fixture(params=["default", "atomic", "radix"])
+def csr_path(request, monkeypatch):
+    """Which of the two builds runs: the library's own choice by size (the
+    counting build below 2^18 edges, the radix build above), or one forced."""
+    if request.param != "default":
+        monkeypatch.setenv("GATTN_CSR_PATH", request.param)
+    return request.param
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 5])
-def test_csr_configs(gsa, cfg):
+def test_csr_configs(gsa, cfg, csr_path):
     c = case(cfg)
+    print(f"csr config {cfg} path {csr_path}", flush=True)
     got = gpu_csr(gsa, c.n, c.wl.src, c.wl.dst)
     for a, b in zip(got, (c.rp, c.ci, c.pe)):
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_csr_shuffled_order(gsa, cfg, csr_path):
+    # the same graphs handed over in a random edge order: the radix build's
+    # stable pass then leaves rows in edge-id order and the row sort runs
+    c = case(cfg)
+    perm = np.random.default_rng(cfg).permutation(c.wl.nnz)
+    print(f"csr shuffled config {cfg} path {csr_path}", flush=True)
+    assert_csr_equal(gsa, c.n, c.wl.src[perm], c.wl.dst[perm])
+
+
+@pytest.mark.parametrize("order", ["by_source", "shuffled"])
+def test_csr_radix_large_tiles(gsa, order):
+    # above 2^23 edges the radix passes take 7168-key tiles
+    g = np.random.default_rng(11)
+    n, m = 1_500_000, 9_000_000
+    dst = (g.lognormal(1.5, 1.0, m) * 1000).astype(np.int64) % n
+    src = g.integers(0, n, m)
+    if order == "by_source":
+        o = np.argsort(src, kind="stable")
+        src, dst = src[o], dst[o]
+    print(f"csr radix large tiles, {order}", flush=True)
+    assert_csr_equal(gsa, n, src.astype(np.int32), dst.astype(np.int32))
+
+
+@pytest.mark.parametrize("n", [1, 255, 256, 65535, 65536, 1 << 24])
+def test_csr_radix_digit_counts(gsa, n, monkeypatch):
+    # node counts at the edges of 1, 2, 3 and 4 radix passes; rows of every
+    # length from 0 up, long runs of empty rows, sorted and unsorted sources
+    monkeypatch.setenv("GATTN_CSR_PATH", "radix")
+    g = np.random.default_rng(n)
+    m = 20000
+    dst = (np.minimum(g.zipf(1.5, m) - 1, n - 1).astype(np.int64) * 7919 % n).astype(np.int32)
+    src = g.integers(0, n, m).astype(np.int32)
+    print(f"csr radix n={n}", flush=True)
+    assert_csr_equal(gsa, n, np.sort(src), dst[np.argsort(src, kind="stable")])
+    assert_csr_equal(gsa, n, src, dst)
+
+
 @pytest.mark.slow
-def test_csr_config4(gsa):
+def test_csr_config4(gsa, csr_path):
     c = case(4)
+    print(f"csr config 4 path {csr_path}", flush=True)
     rp, ci, pe = gsa.gattn_build_csr(c.src, c.dst, c.n)
     assert np.array_equal(to_np(rp), c.rp)
     assert np.array_equal(to_np(ci), c.ci)
@@ -53,13 +102,13 @@ def test_csr_config4(gsa):
 
 
 @pytest.mark.parametrize("seed", range(8))
-def test_csr_fuzz(gsa, seed):
+def test_csr_fuzz(gsa, seed, csr_path):
     n = [1, 2, 17, 64, 100, 1000, 3, 500][seed]
     src, dst = W.random_graph(500 + seed, seed, n, [5, 70, 40, 66, 130, 20, 1, 90][seed], multi=seed % 2 == 1)
     assert_csr_equal(gsa, n, src, dst)
 
 
-def test_csr_long_rows(gsa):
+def test_csr_long_rows(gsa, csr_path):
     # one destination above the LDS sort capacity (chunks ranked by binary search),
     # rows of exactly 64 and 65 in-edges, and isolated nodes
     g = np.random.default_rng(3)
@@ -71,7 +120,7 @@ def test_csr_long_rows(gsa):
     assert_csr_equal(gsa, n, src[perm], dst[perm])
 
 
-def test_csr_empty_and_bad(gsa):
+def test_csr_empty_and_bad(gsa, csr_path):
     for n in (0, 5):
         rp, ci, pe = gpu_csr(gsa, n, np.zeros(0, np.int32), np.zeros(0, np.int32))
         assert rp.tolist() == [0] * (n + 1) and ci.size == 0
