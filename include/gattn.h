@@ -141,10 +141,10 @@ GATTN_API gattn_status gattn_build_csr(int32_t num_nodes, int64_t nnz, const int
  *   checks the graph (BAD_GRAPH, DUPLICATE_EDGE), synchronizes `stream` and
  *   stores the total column count in *num_cols [host].  Call 2: *num_cols [host]
  *   holds the capacity of win_cols [num_cols] and tile_mask [num_cols] (uint16,
- *   i.e. num_cols/16 tiles x 16 rows); it needs win_col_ptr from call 1
- *   unchanged, returns BUFFER_TOO_SMALL when the capacity is below
- *   win_col_ptr[W] (read back with one small synchronous copy), then
- *   enqueues the fill.
+ *   i.e. num_cols/16 tiles x 16 rows); it needs win_col_ptr and the workspace
+ *   from call 1 unchanged (call 1 leaves every window's sorted keys there),
+ *   returns BUFFER_TOO_SMALL when the capacity is below win_col_ptr[W] (read
+ *   back with one small synchronous copy), then enqueues the fill.
  *   workspace: at least gattn_build_rowwindows_workspace() bytes (256-B aligned).
  * ------------------------------------------------------------------------ */
 GATTN_API gattn_status gattn_build_rowwindows_workspace(int32_t num_nodes, int64_t nnz, size_t* bytes /*[host]*/);

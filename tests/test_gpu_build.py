@@ -180,6 +180,29 @@ def test_rowwindows_fuzz(gsa, seed):
         assert np.array_equal(a, b.reshape(a.shape))
 
 
+def test_rowwindows_mixed_spans(gsa):
+    # windows whose sources span less than 4096 values (bitmap) next to windows
+    # spanning the whole graph (sorted keys), spans right at the threshold, and
+    # windows whose masks do not fit the LDS assembly (> 2048 columns)
+    g = np.random.default_rng(21)
+    n = 40000
+    srcs, dsts = [], []
+    for r in range(0, 16):            # window 0: sources within 4095 of each other
+        s = g.choice(4096, 30, replace=False) + 1000
+        srcs.append(s); dsts.append(np.full(30, r))
+    srcs.append(np.array([5000, 5000 + 4095])); dsts.append(np.array([16, 17]))   # span 4096 -> sorted keys
+    srcs.append(np.array([7000, 7000 + 4094])); dsts.append(np.array([32, 33]))   # span 4095 -> bitmap
+    for r in range(48, 64):           # window 3: 16 x 200 random sources, > 2048 columns
+        s = g.choice(n, 200, replace=False)
+        srcs.append(s); dsts.append(np.full(200, r))
+    for r in range(64, 80):           # window 4: narrow again
+        s = g.choice(100, 12, replace=False) + 30000
+        srcs.append(s); dsts.append(np.full(12, r))
+    src, dst = np.concatenate(srcs).astype(np.int32), np.concatenate(dsts).astype(np.int32)
+    rp, ci, _ = oracle.build_csr(n, src, dst)
+    assert_rw_equal(gsa, n, rp, ci)
+
+
 def test_rowwindows_long_window(gsa):
     # a window with more than 8192 edges takes the chunked workspace sort
     n = 20000
@@ -196,9 +219,13 @@ def test_rowwindows_long_window(gsa):
     assert_rw_equal(gsa, n, rp, ci)
 
 
-def test_rowwindows_errors(gsa):
-    n = 40
-    src, dst = W.random_graph(700, 0, n, 10)
+@pytest.mark.parametrize("n", [40, 50000])
+def test_rowwindows_errors(gsa, n):
+    # n = 40: every window's sources span < 4096 values (bitmap path); n = 50000:
+    # random sources span more (sorted-key path) -- both must find the repeat
+    src, dst = W.random_graph(700, 0, 40, 10)
+    if n > 40:
+        src = (src.astype(np.int64) * 1237 % n).astype(np.int32)
     src, dst = np.append(src, src[0]).astype(np.int32), np.append(dst, dst[0]).astype(np.int32)
     rp, ci, _ = oracle.build_csr(n, src, dst)
     with pytest.raises(gsa.GattnError) as ei:
