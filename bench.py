@@ -10,9 +10,13 @@ projection), the setting of the gattn-triton article's headline table.
 
 Honest HBM numbers: the step cycles through R copies of the batch whose
 total size is well above the 256 MB Infinity Cache, so every step streams
-its inputs from HBM.  Before the timed region a sleep kernel holds the GPU
-while the host enqueues all K steps, so the GPU then runs them back to back
-and the HIP events around each kernel measure the kernel, not host gaps.
+its inputs from HBM.  Before a timed region a sleep kernel holds the GPU
+while the host enqueues all K steps, so the GPU then runs them back to back.
+Two timed regions of K steps each: the first has events only at its two ends
+and gives the throughput (an event recorded between kernels costs the GPU a
+few microseconds, a fifth of a small step); the second records HIP events
+around the CSR build and around the op of every step, and their averages give
+the per-kernel durations of the roofline.
 
 Output: one JSON line (metric, value in GEdges/s of the whole step, roofline
 of the forward kernel against 8 TB/s HBM, the CPU oracle's rate on the host).
@@ -74,6 +78,8 @@ def parse():
     p.add_argument("--variant", default="forward", choices=list(VARIANTS))
     p.add_argument("--partition", default="node", choices=["balanced", "node"],
                    help="gather path: edge-balanced workgroups with cut heavy rows (workspace) or equal node counts")
+    p.add_argument("--pipeline", action="store_true",
+                   help="build the CSR of batch i+1 on a second stream while batch i runs its forward")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bound of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--counters-run", action="store_true")
@@ -322,18 +328,45 @@ def main():
     use_rw = args.variant == "forward" and (args.path in ("mfma", "hybrid") or (
         args.path == "auto" and wl.dtype != "f32" and wl.mode == "standard" and not wl.has_e))
 
+    main_stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream() if args.pipeline else None        # default priority
+    built = [torch.cuda.Event() for _ in range(R)]
+    used = [torch.cuda.Event() for _ in range(R)]
+
     def step(i, ev=None):
         b = batches[i % R]
+        if side is None:
+            if ev is not None:
+                ev[0].record()
+            rp, ci, pe = b.csr(b.src, b.dst)
+            if use_rw:
+                plans(b, rp, ci)
+            if ev is not None:
+                ev[1].record()
+            run_op(b, rp, ci, pe)
+            if ev is not None:
+                ev[2].record()
+            return
+        # pipelined: the side stream builds batch i's CSR once the forward that
+        # last read this batch slot (step i - R) is done; the main stream waits
+        # for the build, then runs the forward
+        with torch.cuda.stream(side):
+            side.wait_event(used[i % R])
+            if ev is not None:
+                ev[0].record(side)
+            rp, ci, pe = b.csr(b.src, b.dst)
+            if use_rw:
+                plans(b, rp, ci)
+            if ev is not None:
+                ev[3].record(side)
+            built[i % R].record(side)
+        main_stream.wait_event(built[i % R])
         if ev is not None:
-            ev[0].record()
-        rp, ci, pe = b.csr(b.src, b.dst)
-        if use_rw:
-            plans(b, rp, ci)
-        if ev is not None:
-            ev[1].record()
+            ev[1].record(main_stream)
         run_op(b, rp, ci, pe)
         if ev is not None:
-            ev[2].record()
+            ev[2].record(main_stream)
+        used[i % R].record(main_stream)
 
     # warmup (also builds the row windows of every batch)
     for i in range(max(args.warmup, R)):
@@ -353,18 +386,30 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    sleep_s = 1.5 * enqueue_s * K + 2e-3
-    torch.cuda._sleep(int(sleep_s * 2.4e9))
-    start.record()
-    for i in range(K):
-        step(i, evs[i])
-    end.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    build_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+
+    def timed(evs):
+        """K steps behind a sleep that lasts until the host has enqueued them
+        all; returns the start-to-end time of the K steps in ms."""
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        sleep_s = 1.5 * enqueue_s * K + 2e-3
+        torch.cuda._sleep(int(sleep_s * 2.4e9))
+        start.record()
+        if side is not None:
+            side.wait_event(start)      # no build starts before the timed region
+        for i in range(K):
+            step(i, evs[i] if evs else None)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end)
+
+    # throughput: the K steps alone (an event record between kernels costs the
+    # GPU several microseconds, so the per-kernel events get their own run)
+    total_ms = timed(None)
+    # kernel durations: the same K steps with events around the build and the op
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    evented_ms = timed(evs)
+    build_ms = float(np.mean([e[0].elapsed_time(e[3] if side is not None else e[1]) for e in evs]))
     fwd_ms_all = np.array([e[1].elapsed_time(e[2]) for e in evs])
     fwd_ms = float(np.mean(fwd_ms_all))
     ms_per_step = total_ms / K
@@ -389,11 +434,14 @@ def main():
                       "softmax": "none (given weights)" if args.variant == "aggregate" else wl.mode,
                       "edge_projection": wl.has_e and args.variant != "aggregate",
                       "step": f"gattn_build_csr + {VARIANTS[args.variant]}", "variant": args.variant,
+                      "pipeline": ("CSR build of batch i+1 on a second stream during the forward of batch i"
+                                   if side is not None else None),
                       "partition": args.partition if path == "gather" else None,
                       "forward_path": path,
                       "rotating_batches": R},
            "roofline": roofline,
            "forward_gedges_per_s": round(nnz / (fwd_ms * 1e-3) / 1e9, 4),
+           "ms_per_step_with_kernel_events": round(evented_ms / K, 5),
            "build_csr_ms": round(build_ms, 5)}
     if not args.no_cpu:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
