@@ -424,7 +424,8 @@ def main():
                 "traffic": (round(tr["hbm_bytes_per_launch"]) if tr and tr.get("hbm_bytes_per_launch") else None),
                 "kernel": {"gather": "gather_kernel", "mfma": "mfma_kernel", "hybrid": "mfma_kernel + gather_kernel"}[pk],
                 "algorithmic_bytes_per_launch": bmin, "bytes_per_edge": round(bmin / nnz, 2),
-                "kernel_ms": round(fwd_ms, 5), "kernel_ms_min": round(float(fwd_ms_all.min()), 5)}
+                "kernel_ms": round(fwd_ms, 5), "kernel_ms_median": round(float(np.median(fwd_ms_all)), 5),
+                "kernel_ms_min": round(float(fwd_ms_all.min()), 5)}
     res = {"metric": METRIC, "value": round(nnz / (ms_per_step * 1e-3) / 1e9, 4), "unit": "GEdges/s",
            "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
@@ -441,6 +442,7 @@ def main():
                       "rotating_batches": R},
            "roofline": roofline,
            "forward_gedges_per_s": round(nnz / (fwd_ms * 1e-3) / 1e9, 4),
+           "gedge_heads_per_s": round(nnz * wl.heads / (ms_per_step * 1e-3) / 1e9, 4),
            "ms_per_step_with_kernel_events": round(evented_ms / K, 5),
            "build_csr_ms": round(build_ms, 5)}
     if not args.no_cpu:
