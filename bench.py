@@ -251,7 +251,16 @@ def ingest_counters(dirname, config, path_key, variant="forward", partition="nod
            "kernel_source_sha256_16": src_hash(path_key),
            "fetch_kib_per_dispatch": res.get("fwd_FETCH_SIZE"), "write_kib_per_dispatch": res.get("fwd_WRITE_SIZE"),
            "copy_fetch_kib": copy_read, "copy_write_kib": copy_write, "copy_bytes_each_way": COPY_BYTES,
-           "read_scale": fr, "write_scale": fw}
+           "read_scale": fr, "write_scale": fw,
+           "commands": [f"rocprofv3 --pmc {ctr} -d {os.path.join(dirname, ctr.split('_')[0].lower())} -o run "
+                        f"--output-format csv -- python -u bench.py --config {config} --path {path_key}"
+                        + (f" --variant {variant}" if variant != "forward" else "")
+                        + (" --partition balanced" if partition == "balanced" and path_key == "gather" else "")
+                        + " --counters-run" for ctr in ("FETCH_SIZE", "WRITE_SIZE")]
+                       + [f"python bench.py --config {config} --path {path_key}"
+                          + (f" --variant {variant}" if variant != "forward" else "")
+                          + (" --partition balanced" if partition == "balanced" and path_key == "gather" else "")
+                          + f" --ingest-counters {dirname}"]}
     if res.get("fwd_FETCH_SIZE") is not None and fr and res.get("fwd_WRITE_SIZE") is not None and fw:
         out["hbm_bytes_per_launch"] = res["fwd_FETCH_SIZE"] * 1024.0 * fr + res["fwd_WRITE_SIZE"] * 1024.0 * fw
     os.makedirs(PROFILES, exist_ok=True)
