@@ -267,6 +267,8 @@ gattn_status gattn_build_rowwindows(int32_t num_nodes, int64_t nnz, const int32_
       return GATTN_ERR_INVALID_VALUE;
     if (workspace_bytes < rowwindows_workspace_bytes(num_nodes, nnz)) return GATTN_ERR_BUFFER_TOO_SMALL;
     const int64_t W = (num_nodes + 15) / 16;
+    // win_col_ptr is int32: its total, at most nnz + 15 W, must fit
+    if (nnz + 15 * W > INT32_MAX) return GATTN_ERR_UNSUPPORTED;
     if (!win_cols) {
       // call 1: sizes and checks; the status lives in the workspace's first 256 bytes
       int32_t* status_dev = (int32_t*)workspace + 1;

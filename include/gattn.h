@@ -146,6 +146,8 @@ GATTN_API gattn_status gattn_build_csr(int32_t num_nodes, int64_t nnz, const int
  *   returns BUFFER_TOO_SMALL when the capacity is below win_col_ptr[W] (read
  *   back with one small synchronous copy), then enqueues the fill.
  *   workspace: at least gattn_build_rowwindows_workspace() bytes (256-B aligned).
+ *   UNSUPPORTED when nnz + 15 * ceil(N/16) exceeds 2^31 - 1 (the int32
+ *   win_col_ptr could not hold every padded column count).
  * ------------------------------------------------------------------------ */
 GATTN_API gattn_status gattn_build_rowwindows_workspace(int32_t num_nodes, int64_t nnz, size_t* bytes /*[host]*/);
 GATTN_API gattn_status gattn_build_rowwindows(int32_t num_nodes, int64_t nnz, const int32_t* row_ptr,

@@ -218,6 +218,11 @@ def test_build_argument_errors(gsa):
     assert L.gattn_build_rowwindows(10, 20, p(1), p(2), p(3), None, None, None, p(6), need, None) == 1
     assert L.gattn_build_rowwindows(10, 20, None, p(2), p(3), None, None, ctypes.byref(nc), p(6), need, None) == 1
     assert L.gattn_build_rowwindows(10, 20, p(1), p(2), p(3), None, None, ctypes.byref(nc), p(6), need - 8, None) == 5
+    # padded column counts that an int32 win_col_ptr could not hold
+    n_big, m_big = 1 << 27, (1 << 31) - (1 << 20)
+    assert L.gattn_build_rowwindows_workspace(n_big, m_big, ctypes.byref(sz)) == 0
+    assert L.gattn_build_rowwindows(n_big, m_big, p(1), p(2), p(3), None, None, ctypes.byref(nc), p(6), sz.value,
+                                    None) == gsa.GATTN_ERR_UNSUPPORTED
 
 
 def test_csr_workspace_per_build(gsa, monkeypatch):
