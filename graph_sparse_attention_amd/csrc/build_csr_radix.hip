@@ -11,7 +11,8 @@
 //   histogram  digit counts of every pass in one read of src/dst (LDS
 //              histograms, one global add per digit and workgroup); flags a
 //              bad index and whether src is non-decreasing
-//   pass x P   one launch per digit of at most 8 bits.  A 4096-key tile ranks
+//   pass x P   one launch per digit of at most 8 bits (9 where that saves a
+//              pass; 512 buckets then).  A 4096-key tile ranks
 //              its keys stably inside each wave (ballot peer masks over the
 //              digit bits, one LDS counter per digit and wave), learns the
 //              global start of each digit from the histogram plus the tiles
@@ -35,7 +36,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kRadix = 256;               // buckets per pass: digits of at most 8 bits
+constexpr int kRadixMax = 512;            // buckets per pass: digits of at most 9 bits
 // keys per thread: 16 (4096-key tiles) up to 2^23 edges, 28 (7168-key tiles)
 // above, where longer digit runs write better and the extra tiles' latency
 // matters less (28 x 12 bytes of keys and values per thread stay in registers)
@@ -59,11 +60,13 @@ struct Digits {
 };
 
 // keys are 0..n (n marks an invalid edge): B = bit length of n, split as
-// evenly as possible into ceil(B / 8) digits, lowest first
+// evenly as possible into ceil(B / 8) digits, lowest first -- or ceil(B / 9)
+// digits of up to 9 bits (512 buckets) when that is one pass fewer (B = 17,
+// 18, 25..27)
 Digits digits_of(int32_t n) {
   const int B = 32 - __builtin_clz((uint32_t)n);
   Digits d{};
-  d.passes = (B + 7) / 8;
+  d.passes = std::min((B + 7) / 8, (B + 8) / 9);
   int s = 0;
   for (int p = 0; p < d.passes; ++p) {
     d.bits[p] = B / d.passes + (p < B % d.passes ? 1 : 0);
@@ -73,12 +76,19 @@ Digits digits_of(int32_t n) {
   return d;
 }
 
+// buckets of the passes: 512 when some digit has 9 bits
+int radix_of(const Digits& d) {
+  for (int p = 0; p < d.passes; ++p)
+    if (d.bits[p] > 8) return 512;
+  return 256;
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct RadixWs {
   int32_t* flags;     // [64]
-  uint32_t* hist;     // [kMaxPasses][kRadix]
-  uint64_t* status;   // [passes][tiles][kRadix]
+  uint32_t* hist;     // [kMaxPasses][kRadixMax]
+  uint64_t* status;   // [passes][tiles][radix]
   uint32_t* keys[2];  // [nnz] each
   uint64_t* vals[2];  // [nnz] each
   int64_t clear_ints; // flags + hist + status, cleared in one launch
@@ -96,9 +106,9 @@ RadixWs carve(void* ws, int32_t n, int64_t nnz) {
   w.flags = (int32_t*)p;
   p += 256;
   w.hist = (uint32_t*)p;
-  p += align256(sizeof(uint32_t) * kMaxPasses * kRadix);
+  p += align256(sizeof(uint32_t) * kMaxPasses * kRadixMax);
   w.status = (uint64_t*)p;
-  p += align256(sizeof(uint64_t) * dg.passes * w.tiles * kRadix);
+  p += align256(sizeof(uint64_t) * dg.passes * w.tiles * radix_of(dg));
   w.clear_ints = (p - (uint8_t*)ws) / 4;
   for (int b = 0; b < 2; ++b) {
     w.keys[b] = (uint32_t*)p;
@@ -145,8 +155,8 @@ __global__ __launch_bounds__(kThreads) void radix_hist_kernel(const int32_t* __r
                                                               int32_t n, Digits dg, uint32_t* __restrict__ hist,
                                                               int32_t* __restrict__ flags,
                                                               int32_t* __restrict__ status_dev) {
-  __shared__ uint32_t h[kMaxPasses * kRadix];
-  for (int i = threadIdx.x; i < kMaxPasses * kRadix; i += kThreads) h[i] = 0;
+  __shared__ uint32_t h[kMaxPasses * kRadixMax];
+  for (int i = threadIdx.x; i < kMaxPasses * kRadixMax; i += kThreads) h[i] = 0;
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t last = nnz - 1, stride = (int64_t)gridDim.x * (kThreads * kHistItems);
@@ -168,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void radix_hist_kernel(const int32_t* __r
       const uint32_t key = edge_key(sv[k], dv[k], n);
       bad |= key == (uint32_t)n;
       unsorted |= e > 0 && prev > sv[k];
-      for (int p = 0; p < dg.passes; ++p) atomicAdd(&h[p * kRadix + digit(key, dg.shift[p], dg.bits[p])], 1u);
+      for (int p = 0; p < dg.passes; ++p) atomicAdd(&h[p * kRadixMax + digit(key, dg.shift[p], dg.bits[p])], 1u);
     }
 #pragma unroll
     for (int k = 0; k < kHistItems; ++k) {
@@ -183,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void radix_hist_kernel(const int32_t* __r
   }
   if (unsorted) flags[kUnsorted] = 1;
   __syncthreads();
-  for (int i = threadIdx.x; i < dg.passes * kRadix; i += kThreads) {
+  for (int i = threadIdx.x; i < dg.passes * kRadixMax; i += kThreads) {
     const uint32_t v = h[i];
     if (v) atomicAdd(&hist[i], v);
   }
@@ -198,8 +208,8 @@ struct PassArgs {
   uint64_t* vout;
   int32_t* col_idx;     // last pass, sources non-decreasing: written directly
   int32_t* edge_perm;
-  const uint32_t* hist;  // [kRadix] global digit counts of this pass
-  uint64_t* status;      // [tiles][kRadix]
+  const uint32_t* hist;  // [radix] global digit counts of this pass
+  uint64_t* status;      // [tiles][radix]
   int32_t* ticket;
   int32_t* flags;
   int32_t* status_dev;
@@ -243,10 +253,12 @@ __device__ __forceinline__ void block_excl_scan2(uint32_t a, uint32_t b, uint32_
 
 // One tile of one pass.  Key j of the tile (j = wave * 1024 + item * 64 +
 // lane) keeps its order among equal digits: a wave ranks its items in item
-// order, lanes in lane order, and waves follow each other.
-template <int kItems, bool FIRST, bool LAST>
+// order, lanes in lane order, and waves follow each other.  Thread t owns
+// the kRadix / 256 consecutive digits from t * kRadix / 256 on.
+template <int kItems, int kRadix, bool FIRST, bool LAST>
 __global__ __launch_bounds__(kThreads) void radix_pass_kernel(PassArgs a) {
   constexpr int kTile = kThreads * kItems;
+  constexpr int DPT = kRadix / kThreads;  // digits per thread
   __shared__ uint64_t s_vals[kTile];  // keys staged first (as 32-bit words), then values
   uint32_t* s_keys = reinterpret_cast<uint32_t*>(s_vals);
   __shared__ uint32_t s_wcnt[kWaves][kRadix];  // per-wave digit counts, then per-wave offsets
@@ -257,7 +269,9 @@ __global__ __launch_bounds__(kThreads) void radix_pass_kernel(PassArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_tile = atomicAdd(a.ticket, 1);
   for (int i = tid; i < kWaves * kRadix; i += kThreads) (&s_wcnt[0][0])[i] = 0;
-  const uint32_t gcount = a.hist[tid];  // this thread's digit: global count
+  uint32_t gcount[DPT];  // this thread's digits: global counts
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) gcount[j] = a.hist[tid * DPT + j];
   __syncthreads();
   const int64_t tile = s_tile;
   const int64_t base = tile * kTile + wave * (kItems * 64) + lane;
@@ -301,57 +315,90 @@ __global__ __launch_bounds__(kThreads) void radix_pass_kernel(PassArgs a) {
   }
   __syncthreads();
 
-  // thread tid owns digit tid: tile count, per-wave offsets, local start
-  uint32_t cnt = 0;
+  // this thread's digits: tile counts, per-wave offsets, local starts
+  uint32_t cnt[DPT], csum = 0, gsum = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t c = s_wcnt[w][tid];
-    s_wcnt[w][tid] = cnt;
-    cnt += c;
+  for (int j = 0; j < DPT; ++j) {
+    const int d = tid * DPT + j;
+    cnt[j] = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t c = s_wcnt[w][d];
+      s_wcnt[w][d] = cnt[j];
+      cnt[j] += c;
+    }
+    publish(a.status + tile * kRadix + d, tile == 0 ? kFlagPrefix : kFlagAggregate, cnt[j]);
+    csum += cnt[j];
+    gsum += gcount[j];
   }
-  uint64_t* st = a.status + tile * kRadix + tid;
-  publish(st, tile == 0 ? kFlagPrefix : kFlagAggregate, cnt);
-  uint32_t start, gbase;
-  block_excl_scan2(cnt, gcount, &start, &gbase, s_scan);
-  s_start[tid] = start;
+  uint32_t start0, gbase0;
+  block_excl_scan2(csum, gsum, &start0, &gbase0, s_scan);
+  uint32_t start[DPT], gbase[DPT];
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) {
+    start[j] = start0;
+    gbase[j] = gbase0;
+    start0 += cnt[j];
+    gbase0 += gcount[j];
+    s_start[tid * DPT + j] = start[j];
+  }
 
-  // decoupled look-back over the earlier tiles of this digit, kLookback
-  // status words per round (tile 0 always holds an inclusive prefix)
-  uint32_t prefix = 0;
+  // decoupled look-back over the earlier tiles of each of this thread's
+  // digits, kLookback status words per digit and round (tile 0 always holds
+  // an inclusive prefix); the digits' walks run side by side
+  uint32_t prefix[DPT];
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) prefix[j] = 0;
   if (tile > 0) {
-    int64_t j = tile - 1;
+    int64_t pos[DPT];
+    bool done[DPT];
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) {
+      pos[j] = tile - 1;
+      done[j] = false;
+    }
     int spins = 0;
     while (true) {
-      uint64_t w[kLookback];
+      uint64_t w[DPT][kLookback];
 #pragma unroll
-      for (int q = 0; q < kLookback; ++q) {
-        const int64_t jj = j - q;
-        const uint64_t x =
-            __hip_atomic_load(a.status + (jj > 0 ? jj : 0) * kRadix + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        w[q] = jj >= 0 ? x : ((uint64_t)kFlagPrefix << 32);
-      }
-      int used = 0;
-      bool done = false;
+      for (int j = 0; j < DPT; ++j)
 #pragma unroll
-      for (int q = 0; q < kLookback; ++q) {
-        if (done || used < q) break;
-        const uint32_t flag = (uint32_t)(w[q] >> 32);
-        if (flag == 0) break;
-        prefix += (uint32_t)w[q];
-        used = q + 1;
-        done = flag == kFlagPrefix;
+        for (int q = 0; q < kLookback; ++q) {
+          const int64_t jj = pos[j] - q;
+          const uint64_t x = __hip_atomic_load(a.status + (jj > 0 ? jj : 0) * kRadix + tid * DPT + j,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          w[j][q] = (jj >= 0 && !done[j]) ? x : ((uint64_t)kFlagPrefix << 32);
+        }
+      bool all = true, moved = false;
+#pragma unroll
+      for (int j = 0; j < DPT; ++j) {
+        if (done[j]) continue;
+        int used = 0;
+#pragma unroll
+        for (int q = 0; q < kLookback; ++q) {
+          if (done[j] || used < q) break;
+          const uint32_t flag = (uint32_t)(w[j][q] >> 32);
+          if (flag == 0) break;
+          prefix[j] += (uint32_t)w[j][q];
+          used = q + 1;
+          done[j] = flag == kFlagPrefix;
+        }
+        pos[j] -= used;
+        moved = moved || used > 0;
+        all = all && done[j];
       }
-      if (done) break;
-      if (used == 0 && ++spins > kSpinLimit) {
+      if (all) break;
+      if (!moved && ++spins > kSpinLimit) {
         a.flags[kErr] = 1;
         if (a.status_dev) *a.status_dev = GATTN_ERR_HIP;
         break;
       }
-      j -= used;
     }
-    publish(st, kFlagPrefix, prefix + cnt);
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) publish(a.status + tile * kRadix + tid * DPT + j, kFlagPrefix, prefix[j] + cnt[j]);
   }
-  s_goff[tid] = gbase + prefix - start;  // modulo 2^32; positions stay below 2^31
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) s_goff[tid * DPT + j] = gbase[j] + prefix[j] - start[j];  // modulo 2^32
   __syncthreads();
 
   // stage the tile in digit order, then write digit runs
@@ -442,12 +489,12 @@ __global__ __launch_bounds__(256) void radix_rowptr_kernel(const uint32_t* __res
   }
 }
 
-template <int kItems>
+template <int kItems, int kRadix>
 void launch_pass(bool first, bool lastp, dim3 grid, dim3 block, const PassArgs& a, hipStream_t s) {
-  if (first && lastp) hipLaunchKernelGGL((radix_pass_kernel<kItems, true, true>), grid, block, 0, s, a);
-  else if (first) hipLaunchKernelGGL((radix_pass_kernel<kItems, true, false>), grid, block, 0, s, a);
-  else if (lastp) hipLaunchKernelGGL((radix_pass_kernel<kItems, false, true>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((radix_pass_kernel<kItems, false, false>), grid, block, 0, s, a);
+  if (first && lastp) hipLaunchKernelGGL((radix_pass_kernel<kItems, kRadix, true, true>), grid, block, 0, s, a);
+  else if (first) hipLaunchKernelGGL((radix_pass_kernel<kItems, kRadix, true, false>), grid, block, 0, s, a);
+  else if (lastp) hipLaunchKernelGGL((radix_pass_kernel<kItems, kRadix, false, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((radix_pass_kernel<kItems, kRadix, false, false>), grid, block, 0, s, a);
 }
 
 }  // namespace
@@ -455,8 +502,8 @@ void launch_pass(bool first, bool lastp, dim3 grid, dim3 block, const PassArgs& 
 size_t build_csr_radix_workspace_bytes(int32_t n, int64_t nnz) {
   const Digits dg = digits_of(std::max(n, 1));
   const int64_t tiles = tiles_of(nnz);
-  return 256 + align256(sizeof(uint32_t) * kMaxPasses * kRadix) +
-         align256(sizeof(uint64_t) * dg.passes * tiles * kRadix) + 2 * align256(sizeof(uint32_t) * nnz) +
+  return 256 + align256(sizeof(uint32_t) * kMaxPasses * kRadixMax) +
+         align256(sizeof(uint64_t) * dg.passes * tiles * radix_of(dg)) + 2 * align256(sizeof(uint32_t) * nnz) +
          2 * align256(sizeof(uint64_t) * nnz);
 }
 
@@ -465,6 +512,7 @@ hipError_t launch_build_csr_radix(int32_t n, int64_t nnz, const int32_t* src, co
                                   hipStream_t s) {
   if (n < 1 || nnz < 1) return hipErrorInvalidValue;
   const Digits dg = digits_of(n);
+  const int radix = radix_of(dg);
   RadixWs w = carve(ws, n, nnz);
   const unsigned cblocks = (unsigned)std::min<int64_t>(ceil_div(w.clear_ints, 256), 4096);
   hipLaunchKernelGGL(radix_clear_kernel, dim3(cblocks), dim3(256), 0, s, w.flags, w.clear_ints, status_dev);
@@ -482,8 +530,8 @@ hipError_t launch_build_csr_radix(int32_t n, int64_t nnz, const int32_t* src, co
     a.vout = w.vals[cur ^ 1];
     a.col_idx = col_idx;
     a.edge_perm = edge_perm;
-    a.hist = w.hist + p * kRadix;
-    a.status = w.status + (int64_t)p * w.tiles * kRadix;
+    a.hist = w.hist + p * kRadixMax;
+    a.status = w.status + (int64_t)p * w.tiles * radix;
     a.ticket = &w.flags[kTicket + p];
     a.flags = w.flags;
     a.status_dev = status_dev;
@@ -493,8 +541,13 @@ hipError_t launch_build_csr_radix(int32_t n, int64_t nnz, const int32_t* src, co
     a.bits = dg.bits[p];
     const bool first = p == 0, lastp = p == dg.passes - 1;
     const dim3 grid((unsigned)w.tiles), block(kThreads);
-    if (items_of(nnz) == kItemsLarge) launch_pass<kItemsLarge>(first, lastp, grid, block, a, s);
-    else launch_pass<kItemsSmall>(first, lastp, grid, block, a, s);
+    if (items_of(nnz) == kItemsLarge) {
+      if (radix == 512) launch_pass<kItemsLarge, 512>(first, lastp, grid, block, a, s);
+      else launch_pass<kItemsLarge, 256>(first, lastp, grid, block, a, s);
+    } else {
+      if (radix == 512) launch_pass<kItemsSmall, 512>(first, lastp, grid, block, a, s);
+      else launch_pass<kItemsSmall, 256>(first, lastp, grid, block, a, s);
+    }
     cur ^= 1;
   }
   const unsigned rblocks = (unsigned)std::min<int64_t>(ceil_div(nnz + 1, 256 * 8), 4096);

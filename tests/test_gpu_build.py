@@ -77,10 +77,12 @@ def test_csr_radix_large_tiles(gsa, order):
     assert_csr_equal(gsa, n, src.astype(np.int32), dst.astype(np.int32))
 
 
-@pytest.mark.parametrize("n", [1, 255, 256, 65535, 65536, 1 << 24])
+@pytest.mark.parametrize("n", [1, 255, 256, 65535, 65536, (1 << 18) - 1, 1 << 18, 1 << 24, (1 << 27) - 1])
 def test_csr_radix_digit_counts(gsa, n, monkeypatch):
-    # node counts at the edges of 1, 2, 3 and 4 radix passes; rows of every
-    # length from 0 up, long runs of empty rows, sorted and unsorted sources
+    # node counts at the edges of 1, 2, 3 and 4 radix passes, with 8-bit digits
+    # and with the 9-bit digits (512 buckets) that save a pass for 17, 18 and
+    # 25-27-bit keys; rows of every length from 0 up, long runs of empty rows,
+    # sorted and unsorted sources
     monkeypatch.setenv("GATTN_CSR_PATH", "radix")
     g = np.random.default_rng(n)
     m = 20000
