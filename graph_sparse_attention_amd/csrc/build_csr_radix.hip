@@ -12,13 +12,14 @@
 //              histograms, one global add per digit and workgroup); flags a
 //              bad index and whether src is non-decreasing
 //   pass x P   one launch per digit of at most 8 bits (9 where that saves a
-//              pass; 512 buckets then).  A 4096-key tile ranks
-//              its keys stably inside each wave (ballot peer masks over the
-//              digit bits, one LDS counter per digit and wave), learns the
-//              global start of each digit from the histogram plus the tiles
-//              before it (decoupled look-back on one 64-bit status word per
-//              tile and digit, tiles taken in ticket order), and writes its
-//              keys digit-run by digit-run through LDS
+//              pass; 512 buckets then).  A tile of 4096 keys (7168 from 2^23
+//              edges) ranks its keys stably inside each wave (ballot peer
+//              masks over the digit bits, one LDS counter per digit and
+//              wave), learns the global start of each digit from the
+//              histogram plus the tiles before it (decoupled look-back on one
+//              64-bit status word per tile and digit, tiles taken in ticket
+//              order), and writes its keys, then its values, digit-run by
+//              digit-run through one LDS buffer
 //   row_ptr    from the boundaries of the sorted destinations
 //   sort rows  only when src was not non-decreasing: the stable sort leaves
 //              each destination's edges in edge-id order, which is (source,
