@@ -53,6 +53,17 @@ def test_csr_configs(gsa, cfg, csr_path):
         assert np.array_equal(a, b)
 
 
+@pytest.mark.slow
+def test_csr_config4_shuffled(gsa):
+    # the large graph in a random edge order: the radix build's stable passes
+    # leave rows in edge-id order, so the row sort runs on 2.45M rows of up
+    # to 5000 keys (chunked ranks above 2048)
+    c = case(4)
+    perm = np.random.default_rng(4).permutation(c.wl.nnz)
+    print("csr config 4 shuffled", flush=True)
+    assert_csr_equal(gsa, c.n, c.wl.src[perm], c.wl.dst[perm])
+
+
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_csr_shuffled_order(gsa, cfg, csr_path):
     # the same graphs handed over in a random edge order: the radix build's
