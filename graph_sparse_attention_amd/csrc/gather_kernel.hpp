@@ -313,6 +313,80 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
     }
   }
   const int qcap = AGG ? 0 : kQLdsBytes / qrow;  // rows whose Q is staged in LDS
+  auto rp_val = [&](int t, int v) {
+    v = min(max(v, 0), nnz_i);
+    if (split && t == nn) v = s_cut[4];
+    if (split && t == 0) v = s_cut[1];
+    return v;
+  };
+
+  // The workgroup's edges [E0, E1) are cut into NS equal contiguous pieces
+  // (phase 1); the bounds come from the global row pointers (the same values
+  // phase 0 stages), so that the first step's loads can be issued before it.
+  const int E0 = __builtin_amdgcn_readfirstlane(rp_val(0, a.row_ptr[n0]));
+  const int E1 = max(E0, (int)__builtin_amdgcn_readfirstlane(rp_val(nn, a.row_ptr[n0 + nn])));
+  const int C = max((E1 - E0 + NS - 1) / NS, 1);
+  const int ps = min(E0 + slot * C, E1);
+  const int pe = min(ps + C, E1);
+  const int plast = max(pe - 1, 0);
+
+  // Addresses: a row of K / V / E / the edge update is rowbytes long (< 4 MB),
+  // and this lane's 16 bytes sit at lane_b inside it (0 for idle lanes, whose
+  // loads are issued like the others and never used).
+  const uint32_t rowbytes = (uint32_t)(rowstride * ESZ);
+  const uint64_t lane_b = active ? (uint64_t)eoff * ESZ : 0;
+  const int hw = active ? head : 0;
+  auto row_ptr16 = [&](const uint8_t* base, int row) -> const uint8_t* {
+    return base + lane_b + (uint64_t)(uint32_t)row * rowbytes;
+  };
+  auto load_e = [&](int row) -> u32x4 {
+    const uint8_t* ptr = row_ptr16(a.e, row);
+    return GATTN_GATHER_E_STREAMING ? ld16_stream(ptr) : ld16(ptr);
+  };
+  auto raw_row = [&](int p) -> int { return a.ids ? a.ids[p] : p; };
+  auto fix_row = [&](int r) -> int { return a.ids ? min(max(r, 0), nnz_i - 1) : r; };
+
+  // The edge loop's prefetch registers: column indices, per-edge rows (edge
+  // ids two steps ahead) and edge tensor rows / weights of the next step.
+  int cN[U], rN[U], rNN[U];
+  u32x4 eN[U];
+  float wN[U];
+  // The first step's loads.  Each side of the (uniform) branch on the edge-id
+  // map issues its own edge row loads: after a join, a use of rows that one
+  // side loaded would make the other side wait for every load in flight
+  // (the Q rows included), since the wait counts are per wave and in order.
+  auto prefetch_first = [&]() {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = min(ps + u, plast);
+      cN[u] = a.col_idx[p];
+      rN[u] = p;
+      rNN[u] = min(ps + U + u, plast);
+      eN[u] = u32x4{0u, 0u, 0u, 0u};
+      wN[u] = 0.f;
+    }
+    if constexpr (ROWS) {
+      auto edge_rows = [&]() {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if constexpr (HAS_E) eN[u] = load_e(rN[u]);
+          if constexpr (AGG) wN[u] = a.w[(int64_t)rN[u] * a.H + hw];
+        }
+      };
+      if (a.ids) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          rN[u] = a.ids[rN[u]];
+          rNN[u] = a.ids[rNN[u]];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) rN[u] = fix_row(rN[u]);
+        edge_rows();
+      } else {
+        edge_rows();
+      }
+    }
+  };
 
   // ---- phase 0: row pointers and Q rows into LDS (one coalesced pass); a
   // range that starts or ends inside a row starts or ends at the cut edge.
@@ -328,12 +402,6 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
     const int li = t / chunks, c = t - li * chunks;
     return reinterpret_cast<u32x4*>(s_q + li * qrow + c * 16);
   };
-  auto rp_val = [&](int t, int v) {
-    v = min(max(v, 0), nnz_i);
-    if (split && t == nn) v = s_cut[4];
-    if (split && t == 0) v = s_cut[1];
-    return v;
-  };
   {
     // addresses clamped into range: no branch around a load, so no merge of
     // its register that would wait for it before the next load is issued
@@ -345,6 +413,10 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
 #pragma unroll
     for (int j = 0; j < kQB; ++j)
       if (tid + j * kGatherThreads < qn) *q_dst(tid + j * kGatherThreads) = qv[j];
+    // the first step's column indices and edge rows, in flight from here on
+    // (issued after the stores above: a wait for Q placed after the branches
+    // of this call would also wait for them)
+    if (nnz_i > 0) prefetch_first();
   }
   for (int t = tid + kGatherThreads; t <= nn; t += kGatherThreads) s_rp[t] = rp_val(t, a.row_ptr[n0 + t]);
   for (int t = tid + kQB * kGatherThreads; t < qn; t += kGatherThreads) *q_dst(t) = ld16(q_src(t));
@@ -357,11 +429,6 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
   }
 
   // ---- phase 1: equal contiguous pieces of the workgroup's edges
-  const int E0 = __builtin_amdgcn_readfirstlane(s_rp[0]);
-  const int E1 = max(E0, __builtin_amdgcn_readfirstlane(s_rp[nn]));
-  const int C = max((E1 - E0 + NS - 1) / NS, 1);
-  const int ps = min(E0 + slot * C, E1);
-  const int pe = min(ps + C, E1);
   int node = 0, nstart = 0, nend = 0;
   bool first_rec = false;   // this slot holds a record [0]
   int rec0_node = -1;
@@ -401,21 +468,6 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
   };
   if (ps < pe) load_q(node);
 
-  // Addresses: a row of K / V / E / the edge update is rowbytes long (< 4 MB),
-  // and this lane's 16 bytes sit at lane_b inside it (0 for idle lanes, whose
-  // loads are issued like the others and never used).
-  const uint32_t rowbytes = (uint32_t)(rowstride * ESZ);
-  const uint64_t lane_b = active ? (uint64_t)eoff * ESZ : 0;
-  const int hw = active ? head : 0;
-  auto row_ptr16 = [&](const uint8_t* base, int row) -> const uint8_t* {
-    return base + lane_b + (uint64_t)(uint32_t)row * rowbytes;
-  };
-  // row of the per-edge tensors for CSR position p (clamped like the sources)
-  auto edge_row = [&](int p) -> int { return a.ids ? min(max(a.ids[p], 0), nnz_i - 1) : p; };
-  auto load_e = [&](int row) -> u32x4 {
-    const uint8_t* ptr = row_ptr16(a.e, row);
-    return GATTN_GATHER_E_STREAMING ? ld16_stream(ptr) : ld16(ptr);
-  };
 
   // a row cut across workgroups always leaves records (merged in phase 3)
   auto flush = [&]() {
@@ -446,9 +498,6 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
   // a branch, so a global load on either side would make every later use
   // wait for all loads in flight: the choice below is workgroup-uniform.
   //  Q_LDS: every destination's Q row is staged in LDS.
-  const int plast = max(pe - 1, 0);
-  auto raw_row = [&](int p) -> int { return a.ids ? a.ids[p] : p; };
-  auto fix_row = [&](int r) -> int { return a.ids ? min(max(r, 0), nnz_i - 1) : r; };
   auto edge_loop = [&](auto q_lds) {
     constexpr bool Q_LDS = decltype(q_lds)::value;
     auto get_q = [&](int nd) {
@@ -458,24 +507,6 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
         load_q(nd);
       }
     };
-    int cN[U], rN[U], rNN[U];
-    u32x4 eN[U];
-    float wN[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int p = min(ps + u, plast);
-      cN[u] = a.col_idx[p];
-      rN[u] = 0;
-      rNN[u] = 0;
-      eN[u] = u32x4{0u, 0u, 0u, 0u};
-      wN[u] = 0.f;
-      if constexpr (ROWS) {
-        rN[u] = fix_row(raw_row(p));
-        rNN[u] = raw_row(min(ps + U + u, plast));
-      }
-      if constexpr (HAS_E) eN[u] = load_e(rN[u]);
-      if constexpr (AGG) wN[u] = a.w[(int64_t)rN[u] * a.H + hw];
-    }
     for (int base = ps; base < pe; base += U) {
       int cols[U], rows[U];
       u32x4 er[U], kr[U], vr[U];
