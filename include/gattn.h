@@ -34,8 +34,10 @@
  *     is enqueued.  Errors of the HIP runtime (no device, launch failure)
  *     return GATTN_ERR_HIP.  No C++ exception crosses the ABI.
  *   - Integer outputs (CSR, row windows) are unique functions of the input:
- *     identical bits on every run.  gattn_forward uses no atomics and no
- *     cross-workgroup communication, so it too is bit-reproducible.
+ *     identical bits on every run.  gattn_forward accumulates with no atomics:
+ *     each destination's edges are folded in a fixed order (with a workspace,
+ *     the partial states of a row cut across workgroups are merged in part
+ *     order), so it too is bit-reproducible.
  */
 #ifndef GATTN_H
 #define GATTN_H
