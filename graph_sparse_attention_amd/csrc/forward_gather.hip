@@ -66,14 +66,17 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Destinations per workgroup for an equal-count partition: about `target`
 // edges each, at most `cap`, and the grid rounded to whole "rounds" of
 // co-resident workgroups (a last, partly filled round would leave most CUs
-// idle while it runs).
+// idle while it runs).  When the cap allows fewer rows than the rounded grid
+// asks for, the grid takes one more round of smaller workgroups rather than a
+// partly filled one.
 int nodes_per_wg(const Problem& p, double target, int cap, int head_blocks, int64_t resident_all) {
   const int64_t per_round = std::max<int64_t>(1, resident_all / head_blocks);
   const double avg = (double)p.nnz / p.n;
   int npw_target = cap;
   if (avg > 0) npw_target = (int)std::min<double>(cap, std::max(1.0, std::ceil(target / avg)));
   const double wgs = (double)ceil_div(p.n, npw_target) * head_blocks;
-  const int64_t rounds = std::max<int64_t>(1, (int64_t)std::llround(wgs / (double)resident_all));
+  int64_t rounds = std::max<int64_t>(1, (int64_t)std::llround(wgs / (double)resident_all));
+  rounds = std::max<int64_t>(rounds, ceil_div(ceil_div(p.n, cap), per_round));
   return (int)std::min<int64_t>(cap, std::max<int64_t>(1, ceil_div(p.n, rounds * per_round)));
 }
 

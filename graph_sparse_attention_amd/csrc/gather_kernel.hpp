@@ -255,13 +255,22 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
   constexpr bool AGG = MODE == kModeAggregate;
   constexpr bool ROWS = HAS_E || AGG;  // per-edge rows are read
 
+  // Partial (m, l, acc) records of destinations cut by piece boundaries:
+  // [0] the first destination of a piece (started in an earlier piece),
+  // written during the edge loop; [1] the last one (continues into a later
+  // piece), written only after it, into the Q staging buffer, which no slot
+  // reads by then.  Sharing that buffer keeps a workgroup's LDS at about
+  // 26 KB for 16-bit types (6 workgroups per CU) instead of 37 KB (4).
+  constexpr int kRec1Bytes = kGatherThreads * (VEC + 2) * (int)sizeof(float);
+  static_assert(AGG || kRec1Bytes <= kQLdsBytes, "records [1] must fit the Q staging buffer");
   __shared__ int32_t s_rp[kMaxNodesPerWg + 1];
-  __shared__ __attribute__((aligned(16))) uint8_t s_q[AGG ? 16 : kQLdsBytes];
-  // partial records: [0] first destination of a piece (started in an earlier
-  // piece), [1] last destination of a piece (continues into a later one)
-  __shared__ float s_pm[2][kGatherThreads];
-  __shared__ float s_pl[2][kGatherThreads];
-  __shared__ float s_pacc[2][kGatherThreads * VEC];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[AGG ? kRec1Bytes : kQLdsBytes];
+  __shared__ float s_pm0[kGatherThreads];
+  __shared__ float s_pl0[kGatherThreads];
+  __shared__ float s_pacc0[kGatherThreads * VEC];
+  float* const s_pacc1 = reinterpret_cast<float*>(s_q);
+  float* const s_pm1 = s_pacc1 + kGatherThreads * VEC;
+  float* const s_pl1 = s_pm1 + kGatherThreads;
   __shared__ int32_t s_cut[6];  // (row, edge, cont) where the range starts and where it ends
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -469,22 +478,28 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
   if (ps < pe) load_q(node);
 
 
-  // a row cut across workgroups always leaves records (merged in phase 3)
-  auto flush = [&]() {
+  // a row cut across workgroups always leaves records (merged in phase 3).
+  // A destination that continues past the piece is its last one, so inside
+  // the loop (after_loop false) only records [0] arise; a [1] there could
+  // only come from a malformed row_ptr and is dropped (the result of such a
+  // graph is unspecified) rather than written over Q rows still in use.
+  auto flush = [&](bool after_loop) {
     const bool started_before = nstart < ps || (split && node == 0 && cont_first);
     const bool continues = nend > pe || (split && node == nn - 1 && cont_last);
     if (!started_before && !continues) {
       if (active) M::store(a, a.out + ((int64_t)(n0 + node) * rowstride + eoff) * ESZ, l, acc);
-    } else {
-      const int r = started_before ? 0 : 1;
-      s_pm[r][rec] = m;
-      s_pl[r][rec] = l;
+    } else if (started_before) {
+      s_pm0[rec] = m;
+      s_pl0[rec] = l;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) s_pacc[r][rec * VEC + i] = acc[i];
-      if (started_before) {
-        first_rec = true;
-        rec0_node = node;
-      }
+      for (int i = 0; i < VEC; ++i) s_pacc0[rec * VEC + i] = acc[i];
+      first_rec = true;
+      rec0_node = node;
+    } else if (after_loop) {
+      s_pm1[rec] = m;
+      s_pl1[rec] = l;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) s_pacc1[rec * VEC + i] = acc[i];
     }
   };
 
@@ -540,7 +555,7 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
         const int p = base + u;
         if (p >= pe) break;
         if (p >= nend) {
-          flush();
+          flush(false);
           while (node < nn - 1) {  // next destination with edges (monotone pointers: one step + empties)
             ++node;
             nstart = nend;
@@ -568,7 +583,8 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
       edge_loop(std::true_type{});  // the node partition stages every Q row
     }
   }
-  if (ps < pe) flush();
+  __syncthreads();  // no slot reads the Q rows any more: records [1] may take their place
+  if (ps < pe) flush(true);
   __syncthreads();
 
   // ---- phase 2: the slot holding a cut destination's last edge merges its pieces
@@ -576,14 +592,14 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
   const bool xwg_last = split && cont_last && nn > 0 && !(nn == 1 && cont_first);
   if (first_rec && s_rp[rec0_node + 1] <= pe && !(rec0_node == 0 && xwg_first) && !(rec0_node == nn - 1 && xwg_last)) {
     const int first_slot = min(max((s_rp[rec0_node] - E0) / C, 0), slot);
-    float mm = s_pm[1][first_slot * G + lig], ll = s_pl[1][first_slot * G + lig], aa[VEC];
+    float mm = s_pm1[first_slot * G + lig], ll = s_pl1[first_slot * G + lig], aa[VEC];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) aa[i] = s_pacc[1][(first_slot * G + lig) * VEC + i];
+    for (int i = 0; i < VEC; ++i) aa[i] = s_pacc1[(first_slot * G + lig) * VEC + i];
     for (int s = first_slot + 1; s <= slot; ++s) {
       float a2[VEC];
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) a2[i] = s_pacc[0][(s * G + lig) * VEC + i];
-      M::fold(mm, ll, aa, s_pm[0][s * G + lig], s_pl[0][s * G + lig], a2);
+      for (int i = 0; i < VEC; ++i) a2[i] = s_pacc0[(s * G + lig) * VEC + i];
+      M::fold(mm, ll, aa, s_pm0[s * G + lig], s_pl0[s * G + lig], a2);
     }
     if (active) M::store(a, a.out + ((int64_t)(n0 + rec0_node) * rowstride + eoff) * ESZ, ll, aa);
   }
@@ -602,15 +618,23 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
     const int t0 = min(max((max(s_rp[nd + 1], s_rp[nd] + 1) - 1 - E0) / C, s0), NS - 1);
     // the first row's records are all "started before"; the last row starts
     // inside slot s0's piece
-    const int r0 = kind == 0 ? 0 : 1;
-    float pm = s_pm[r0][s0 * G + lig], pl = s_pl[r0][s0 * G + lig], pa[VEC];
+    float pm, pl, pa[VEC];
+    if (kind == 0) {
+      pm = s_pm0[s0 * G + lig];
+      pl = s_pl0[s0 * G + lig];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) pa[i] = s_pacc[r0][(s0 * G + lig) * VEC + i];
+      for (int i = 0; i < VEC; ++i) pa[i] = s_pacc0[(s0 * G + lig) * VEC + i];
+    } else {
+      pm = s_pm1[s0 * G + lig];
+      pl = s_pl1[s0 * G + lig];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) pa[i] = s_pacc1[(s0 * G + lig) * VEC + i];
+    }
     for (int sl = s0 + 1; sl <= t0; ++sl) {
       float a2[VEC];
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) a2[i] = s_pacc[0][(sl * G + lig) * VEC + i];
-      M::fold(pm, pl, pa, s_pm[0][sl * G + lig], s_pl[0][sl * G + lig], a2);
+      for (int i = 0; i < VEC; ++i) a2[i] = s_pacc0[(sl * G + lig) * VEC + i];
+      M::fold(pm, pl, pa, s_pm0[sl * G + lig], s_pl0[sl * G + lig], a2);
     }
     const int64_t HB_B = (int64_t)gridDim.y * a.num_wg, hb_B = (int64_t)hb * a.num_wg;
     auto part = [&](int k, int64_t bb) { return (int64_t)k * HB_B + hb_B + bb; };
