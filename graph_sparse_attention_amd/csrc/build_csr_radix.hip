@@ -13,13 +13,14 @@
 //              bad index and whether src is non-decreasing
 //   pass x P   one launch per digit of at most 8 bits (9 where that saves a
 //              pass; 512 buckets then).  A tile of 4096 keys (7168 from 2^23
-//              edges) ranks its keys stably inside each wave (ballot peer
-//              masks over the digit bits, one LDS counter per digit and
-//              wave), learns the global start of each digit from the
-//              histogram plus the tiles before it (decoupled look-back on one
-//              64-bit status word per tile and digit, tiles taken in ticket
-//              order), and writes its keys, then its values, digit-run by
-//              digit-run through one LDS buffer
+//              edges) ranks its keys stably inside each wave (peer groups
+//              matched through one LDS word per digit, one LDS counter per
+//              digit and wave advanced by one atomic per group), learns the
+//              global start of each digit from the histogram plus the tiles
+//              before it (decoupled look-back on one 64-bit status word per
+//              tile and digit, tiles taken in ticket order), and writes its
+//              keys, then its values, digit-run by digit-run through one LDS
+//              buffer
 //   row_ptr    from the boundaries of the sorted destinations
 //   sort rows  only when src was not non-decreasing: the stable sort leaves
 //              each destination's edges in edge-id order, which is (source,
@@ -38,6 +39,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRadixMax = 512;            // buckets per pass: digits of at most 9 bits
+constexpr int kRankGroup = 4;   // items whose LDS atomics of the ranking are in flight together
 // keys per thread: 16 (4096-key tiles) up to 2^23 edges, 28 (7168-key tiles)
 // above, where longer digit runs write better and the extra tiles' latency
 // matters less (28 x 12 bytes of keys and values per thread stay in registers)
@@ -256,8 +258,11 @@ __device__ __forceinline__ void block_excl_scan2(uint32_t a, uint32_t b, uint32_
 // lane) keeps its order among equal digits: a wave ranks its items in item
 // order, lanes in lane order, and waves follow each other.  Thread t owns
 // the kRadix / 256 consecutive digits from t * kRadix / 256 on.
+// The launch bound (2 waves per SIMD) holds the 7168-key tiles to 256
+// registers (a few bytes of spill) instead of the ~270 that would leave one
+// wave per SIMD.
 template <int kItems, int kRadix, bool FIRST, bool LAST>
-__global__ __launch_bounds__(kThreads) void radix_pass_kernel(PassArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void radix_pass_kernel(PassArgs a) {
   constexpr int kTile = kThreads * kItems;
   constexpr int DPT = kRadix / kThreads;  // digits per thread
   __shared__ uint64_t s_vals[kTile];  // keys staged first (as 32-bit words), then values
@@ -270,6 +275,11 @@ __global__ __launch_bounds__(kThreads) void radix_pass_kernel(PassArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_tile = atomicAdd(a.ticket, 1);
   for (int i = tid; i < kWaves * kRadix; i += kThreads) (&s_wcnt[0][0])[i] = 0;
+  // peer-group words, one per digit and wave, in the staging buffer (not
+  // used before the tile is staged)
+  static_assert(kWaves * kRadix <= kTile, "peer words must fit the staging buffer");
+  for (int i = tid; i < kWaves * kRadix; i += kThreads) s_vals[i] = 0;
+  uint64_t* const s_match = s_vals + wave * kRadix;
   uint32_t gcount[DPT];  // this thread's digits: global counts
 #pragma unroll
   for (int j = 0; j < DPT; ++j) gcount[j] = a.hist[tid * DPT + j];
@@ -294,25 +304,50 @@ __global__ __launch_bounds__(kThreads) void radix_pass_kernel(PassArgs a) {
     }
   }
 
-  // stable rank inside the wave, item by item
+  // stable rank inside the wave, item by item: the lanes holding one digit
+  // in item k (its peer group) take the next positions of that digit in lane
+  // order.  The group is found in LDS: each lane ORs its lane bit into the
+  // wave's word for its digit, reads the word back and clears it (a wave's
+  // LDS operations run in issue order, so the read sees every lane's bit and
+  // the next item starts from zero).  The group's lowest lane then advances
+  // the wave's counter of the digit by the group's size with an atomic add,
+  // which sees the counts of all earlier items; the other lanes read the old
+  // count from it.
+  // kRankGroup items are in flight together.
   const uint64_t lanes_below = (1ull << lane) - 1ull;
+  const uint64_t lane_bit = 1ull << lane;
   uint32_t rank[kItems];
 #pragma unroll
-  for (int k = 0; k < kItems; ++k) {
-    const bool valid = base + k * 64 <= last;
-    const uint32_t dg = digit(key[k], a.shift, a.bits);
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < a.bits; ++b) {
-      const bool on = (dg >> b) & 1u;
-      const uint64_t m = __ballot(on);
-      peers &= on ? m : ~m;
+  for (int k0 = 0; k0 < kItems; k0 += kRankGroup) {
+    constexpr int kg = kRankGroup;
+    uint64_t peers[kg];
+    uint32_t dgs[kg];
+#pragma unroll
+    for (int k = k0; k < k0 + kg && k < kItems; ++k) {
+      const uint32_t dg = digit(key[k], a.shift, a.bits);
+      dgs[k - k0] = dg;
+      peers[k - k0] = 0;
+      if (base + k * 64 <= last) {
+        atomicOr(reinterpret_cast<unsigned long long*>(&s_match[dg]), (unsigned long long)lane_bit);
+        peers[k - k0] = s_match[dg];
+        s_match[dg] = 0;
+      }
     }
-    uint32_t old = 0;
-    if (valid) old = s_wcnt[wave][dg];
-    rank[k] = old + (uint32_t)__popcll(peers & lanes_below);
-    // the highest lane of each peer group advances the counter; the wave's
-    // LDS reads of this item are ordered before its writes
-    if (valid && (peers >> lane) == 1ull) s_wcnt[wave][dg] = old + (uint32_t)__popcll(peers);
+    uint32_t old[kg];
+#pragma unroll
+    for (int k = k0; k < k0 + kg && k < kItems; ++k) {
+      const uint64_t pm = peers[k - k0];
+      const bool valid = pm != 0;  // a valid lane is its own peer
+      const uint32_t leader = valid ? (uint32_t)__builtin_ctzll(pm) : (uint32_t)lane;
+      // every lane takes part (the others add 0, which changes nothing), so
+      // no branch holds the atomics back; only the leader's old value is used
+      const uint32_t add = valid && leader == (uint32_t)lane ? (uint32_t)__popcll(pm) : 0u;
+      old[k - k0] = atomicAdd(&s_wcnt[wave][dgs[k - k0]], add);
+      rank[k] = (uint32_t)__popcll(pm & lanes_below) | (leader << 16);
+    }
+#pragma unroll
+    for (int k = k0; k < k0 + kg && k < kItems; ++k)
+      rank[k] = (rank[k] & 0xffffu) + (uint32_t)__shfl((int)old[k - k0], (int)(rank[k] >> 16), 64);
   }
   __syncthreads();
 
