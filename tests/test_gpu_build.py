@@ -133,6 +133,28 @@ def test_csr_long_rows(gsa, csr_path):
     assert_csr_equal(gsa, n, src[perm], dst[perm])
 
 
+@pytest.mark.parametrize("kind", ["star", "four_hubs", "runs"])
+def test_csr_radix_large_peer_groups(gsa, kind, monkeypatch):
+    # many lanes of a wave holding one digit at once: every edge into one node,
+    # edges spread over four destinations, and destinations in runs of 64
+    # (a whole wave's item on one digit), in source order and shuffled
+    monkeypatch.setenv("GATTN_CSR_PATH", "radix")
+    g = np.random.default_rng(11)
+    n, m = 70000, 100000
+    if kind == "star":
+        dst = np.full(m, 12345, np.int64)
+    elif kind == "four_hubs":
+        dst = g.choice(np.array([3, 259, 40000, 69999]), m)
+    else:
+        dst = np.repeat(g.integers(0, n, m // 64 + 1), 64)[:m]
+    src = g.integers(0, n, m)
+    src, dst = src.astype(np.int32), dst.astype(np.int32)
+    print(f"csr radix peer groups {kind}", flush=True)
+    order = np.argsort(src, kind="stable")
+    assert_csr_equal(gsa, n, src[order], dst[order])
+    assert_csr_equal(gsa, n, src, dst)
+
+
 def test_csr_empty_and_bad(gsa, csr_path):
     for n in (0, 5):
         rp, ci, pe = gpu_csr(gsa, n, np.zeros(0, np.int32), np.zeros(0, np.int32))
