@@ -17,8 +17,10 @@
 //              matched through one LDS word per digit, one LDS counter per
 //              digit and wave advanced by one atomic per group), learns the
 //              global start of each digit from the histogram plus the tiles
-//              before it (decoupled look-back on one 64-bit status word per
-//              tile and digit, tiles taken in ticket order), and writes its
+//              before it (two-level decoupled look-back: the earlier tiles
+//              of its group of 16, then the earlier groups, on 64-bit status
+//              words per tile / group and digit, tiles taken in ticket
+//              order), and writes its
 //              keys, then its values, digit-run by digit-run through one LDS
 //              buffer
 //   row_ptr    from the boundaries of the sorted destinations
@@ -45,7 +47,8 @@ constexpr int kRankGroup = 4;   // items whose LDS atomics of the ranking are in
 // matters less (28 x 12 bytes of keys and values per thread stay in registers)
 constexpr int kItemsSmall = 16, kItemsLarge = 28;
 constexpr int64_t kLargeEdges = 1 << 23;
-constexpr int kLookback = 4;  // earlier tiles' status words read per look-back round (8 and 16 were no faster)
+constexpr int kLookback = 4;
+constexpr int kGroup = 16;      // tiles per look-back group  // earlier tiles' status words read per look-back round (8 and 16 were no faster)
 constexpr int kMaxPasses = 4;             // keys of at most 32 bits
 constexpr int kHistBlocks = 2048;
 constexpr int kHistItems = 16;             // edges per thread and round of the histogram
@@ -92,10 +95,11 @@ struct RadixWs {
   int32_t* flags;     // [64]
   uint32_t* hist;     // [kMaxPasses][kRadixMax]
   uint64_t* status;   // [passes][tiles][radix]
+  uint64_t* gstatus;  // [passes][groups][radix]
   uint32_t* keys[2];  // [nnz] each
   uint64_t* vals[2];  // [nnz] each
-  int64_t clear_ints; // flags + hist + status, cleared in one launch
-  int64_t tiles;
+  int64_t clear_ints; // flags + hist + status + gstatus, cleared in one launch
+  int64_t tiles, groups;
 };
 
 int items_of(int64_t nnz) { return nnz >= kLargeEdges ? kItemsLarge : kItemsSmall; }
@@ -112,6 +116,9 @@ RadixWs carve(void* ws, int32_t n, int64_t nnz) {
   p += align256(sizeof(uint32_t) * kMaxPasses * kRadixMax);
   w.status = (uint64_t*)p;
   p += align256(sizeof(uint64_t) * dg.passes * w.tiles * radix_of(dg));
+  w.groups = ceil_div(w.tiles, kGroup);
+  w.gstatus = (uint64_t*)p;
+  p += align256(sizeof(uint64_t) * dg.passes * w.groups * radix_of(dg));
   w.clear_ints = (p - (uint8_t*)ws) / 4;
   for (int b = 0; b < 2; ++b) {
     w.keys[b] = (uint32_t*)p;
@@ -212,7 +219,9 @@ struct PassArgs {
   int32_t* col_idx;     // last pass, sources non-decreasing: written directly
   int32_t* edge_perm;
   const uint32_t* hist;  // [radix] global digit counts of this pass
-  uint64_t* status;      // [tiles][radix]
+  uint64_t* status;      // [tiles][radix] tile aggregates
+  uint64_t* gstatus;     // [groups][radix] group aggregates / inclusive prefixes
+  int64_t tiles;
   int32_t* ticket;
   int32_t* flags;
   int32_t* status_dev;
@@ -264,6 +273,10 @@ __device__ __forceinline__ void block_excl_scan2(uint32_t a, uint32_t b, uint32_
 template <int kItems, int kRadix, bool FIRST, bool LAST>
 __global__ __launch_bounds__(kThreads, 2) void radix_pass_kernel(PassArgs a) {
   constexpr int kTile = kThreads * kItems;
+  // two-level look-back for the 4096-key tiles (inputs of up to ~2^23 edges,
+  // whose tiles mostly run at once); the 7168-key kernel keeps the one-level
+  // walk, which needs fewer registers (it spills less at 256)
+  constexpr bool kTwoLevel = kItems == kItemsSmall;
   constexpr int DPT = kRadix / kThreads;  // digits per thread
   __shared__ uint64_t s_vals[kTile];  // keys staged first (as 32-bit words), then values
   uint32_t* s_keys = reinterpret_cast<uint32_t*>(s_vals);
@@ -363,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 2) void radix_pass_kernel(PassArgs a) {
       s_wcnt[w][d] = cnt[j];
       cnt[j] += c;
     }
-    publish(a.status + tile * kRadix + d, tile == 0 ? kFlagPrefix : kFlagAggregate, cnt[j]);
+    publish(a.status + tile * kRadix + d, !kTwoLevel && tile == 0 ? kFlagPrefix : kFlagAggregate, cnt[j]);
     csum += cnt[j];
     gsum += gcount[j];
   }
@@ -379,21 +392,25 @@ __global__ __launch_bounds__(kThreads, 2) void radix_pass_kernel(PassArgs a) {
     s_start[tid * DPT + j] = start[j];
   }
 
-  // decoupled look-back over the earlier tiles of each of this thread's
-  // digits, kLookback status words per digit and round (tile 0 always holds
-  // an inclusive prefix); the digits' walks run side by side
-  uint32_t prefix[DPT];
-#pragma unroll
-  for (int j = 0; j < DPT; ++j) prefix[j] = 0;
-  if (tile > 0) {
+  // Look-back for each of this thread's digits.  Two levels: tiles form groups
+  // of kGroup consecutive tickets.  A tile sums the aggregates of the earlier
+  // tiles of its group; the group's last tile publishes the group's
+  // aggregate, and later its inclusive prefix; every tile then walks back over
+  // the earlier groups' words, adding aggregates until an inclusive prefix
+  // (group 0's always is one).  Each walk reads kLookback words per digit and
+  // round, the digits' walks side by side.  Every wait is for a lower ticket,
+  // and an empty poll counts towards a bounded limit.
+  int spins = 0;
+  // adds st[pos .. lo] (stopping early at an inclusive prefix) to sum
+  auto walk = [&](const uint64_t* st, int64_t pos0, int64_t lo, uint32_t* sum) {
+    if (pos0 < lo) return;  // nothing before this tile (workgroup-uniform)
     int64_t pos[DPT];
     bool done[DPT];
 #pragma unroll
     for (int j = 0; j < DPT; ++j) {
-      pos[j] = tile - 1;
-      done[j] = false;
+      pos[j] = pos0;
+      done[j] = pos0 < lo;
     }
-    int spins = 0;
     while (true) {
       uint64_t w[DPT][kLookback];
 #pragma unroll
@@ -401,9 +418,9 @@ __global__ __launch_bounds__(kThreads, 2) void radix_pass_kernel(PassArgs a) {
 #pragma unroll
         for (int q = 0; q < kLookback; ++q) {
           const int64_t jj = pos[j] - q;
-          const uint64_t x = __hip_atomic_load(a.status + (jj > 0 ? jj : 0) * kRadix + tid * DPT + j,
+          const uint64_t x = __hip_atomic_load(st + (jj > lo ? jj : lo) * kRadix + tid * DPT + j,
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          w[j][q] = (jj >= 0 && !done[j]) ? x : ((uint64_t)kFlagPrefix << 32);
+          w[j][q] = (jj >= lo && !done[j]) ? x : ((uint64_t)kFlagPrefix << 32);  // past the range: an end of value 0
         }
       bool all = true, moved = false;
 #pragma unroll
@@ -415,7 +432,7 @@ __global__ __launch_bounds__(kThreads, 2) void radix_pass_kernel(PassArgs a) {
           if (done[j] || used < q) break;
           const uint32_t flag = (uint32_t)(w[j][q] >> 32);
           if (flag == 0) break;
-          prefix[j] += (uint32_t)w[j][q];
+          sum[j] += (uint32_t)w[j][q];
           used = q + 1;
           done[j] = flag == kFlagPrefix;
         }
@@ -430,8 +447,38 @@ __global__ __launch_bounds__(kThreads, 2) void radix_pass_kernel(PassArgs a) {
         break;
       }
     }
+  };
+  uint32_t prefix[DPT];
+  if constexpr (kTwoLevel) {
+    const int64_t grp = tile / kGroup, g0 = grp * kGroup;
+    const bool group_last = tile == min(g0 + kGroup, a.tiles) - 1;
+    uint32_t within[DPT], before[DPT];
 #pragma unroll
-    for (int j = 0; j < DPT; ++j) publish(a.status + tile * kRadix + tid * DPT + j, kFlagPrefix, prefix[j] + cnt[j]);
+    for (int j = 0; j < DPT; ++j) within[j] = before[j] = 0;
+    walk(a.status, tile - 1, g0, within);
+    if (group_last) {
+#pragma unroll
+      for (int j = 0; j < DPT; ++j)
+        publish(a.gstatus + grp * kRadix + tid * DPT + j, grp == 0 ? kFlagPrefix : kFlagAggregate, within[j] + cnt[j]);
+    }
+    walk(a.gstatus, grp - 1, 0, before);
+    if (group_last && grp > 0) {
+#pragma unroll
+      for (int j = 0; j < DPT; ++j)
+        publish(a.gstatus + grp * kRadix + tid * DPT + j, kFlagPrefix, before[j] + within[j] + cnt[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) prefix[j] = before[j] + within[j];
+  } else {
+    // one level: back over the earlier tiles (tile 0 holds an inclusive
+    // prefix), then this tile's own inclusive prefix
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) prefix[j] = 0;
+    walk(a.status, tile - 1, 0, prefix);
+    if (tile > 0) {
+#pragma unroll
+      for (int j = 0; j < DPT; ++j) publish(a.status + tile * kRadix + tid * DPT + j, kFlagPrefix, prefix[j] + cnt[j]);
+    }
   }
 #pragma unroll
   for (int j = 0; j < DPT; ++j) s_goff[tid * DPT + j] = gbase[j] + prefix[j] - start[j];  // modulo 2^32
@@ -539,8 +586,9 @@ size_t build_csr_radix_workspace_bytes(int32_t n, int64_t nnz) {
   const Digits dg = digits_of(std::max(n, 1));
   const int64_t tiles = tiles_of(nnz);
   return 256 + align256(sizeof(uint32_t) * kMaxPasses * kRadixMax) +
-         align256(sizeof(uint64_t) * dg.passes * tiles * radix_of(dg)) + 2 * align256(sizeof(uint32_t) * nnz) +
-         2 * align256(sizeof(uint64_t) * nnz);
+         align256(sizeof(uint64_t) * dg.passes * tiles * radix_of(dg)) +
+         align256(sizeof(uint64_t) * dg.passes * ceil_div(tiles, kGroup) * radix_of(dg)) +
+         2 * align256(sizeof(uint32_t) * nnz) + 2 * align256(sizeof(uint64_t) * nnz);
 }
 
 hipError_t launch_build_csr_radix(int32_t n, int64_t nnz, const int32_t* src, const int32_t* dst, int32_t* row_ptr,
@@ -568,6 +616,8 @@ hipError_t launch_build_csr_radix(int32_t n, int64_t nnz, const int32_t* src, co
     a.edge_perm = edge_perm;
     a.hist = w.hist + p * kRadixMax;
     a.status = w.status + (int64_t)p * w.tiles * radix;
+    a.gstatus = w.gstatus + (int64_t)p * w.groups * radix;
+    a.tiles = w.tiles;
     a.ticket = &w.flags[kTicket + p];
     a.flags = w.flags;
     a.status_dev = status_dev;
