@@ -155,6 +155,20 @@ def test_csr_radix_large_peer_groups(gsa, kind, monkeypatch):
     assert_csr_equal(gsa, n, src, dst)
 
 
+@pytest.mark.parametrize("tiles", [1, 15, 16, 17, 32, 33, 48])
+def test_csr_radix_lookback_groups(gsa, tiles, monkeypatch):
+    # the look-back of the 4096-key tiles works in groups of 16 tiles: tile
+    # counts at and around whole groups (a last tile that ends a group, one
+    # that opens a new group alone), with a ragged last tile
+    monkeypatch.setenv("GATTN_CSR_PATH", "radix")
+    g = np.random.default_rng(100 + tiles)
+    n = 50000
+    m = tiles * 4096 - (0 if tiles % 2 else 1000)
+    src, dst = g.integers(0, n, m).astype(np.int32), g.integers(0, n, m).astype(np.int32)
+    print(f"csr radix look-back groups tiles={tiles} m={m}", flush=True)
+    assert_csr_equal(gsa, n, src, dst)
+
+
 def test_csr_empty_and_bad(gsa, csr_path):
     for n in (0, 5):
         rp, ci, pe = gpu_csr(gsa, n, np.zeros(0, np.int32), np.zeros(0, np.int32))
