@@ -169,6 +169,18 @@ def test_csr_radix_lookback_groups(gsa, tiles, monkeypatch):
     assert_csr_equal(gsa, n, src, dst)
 
 
+def test_csr_radix_many_groups(gsa, monkeypatch):
+    # 3M edges: 733 tiles of 4096 keys in 46 look-back groups, more tiles than
+    # are resident at once; a power-law-like destination mix, random order
+    monkeypatch.setenv("GATTN_CSR_PATH", "radix")
+    g = np.random.default_rng(21)
+    n, m = 400000, 3000000
+    dst = (np.minimum(g.zipf(1.7, m) - 1, n - 1).astype(np.int64) * 7919 % n).astype(np.int32)
+    src = g.integers(0, n, m).astype(np.int32)
+    print("csr radix many groups", flush=True)
+    assert_csr_equal(gsa, n, src, dst)
+
+
 def test_csr_empty_and_bad(gsa, csr_path):
     for n in (0, 5):
         rp, ci, pe = gpu_csr(gsa, n, np.zeros(0, np.int32), np.zeros(0, np.int32))
