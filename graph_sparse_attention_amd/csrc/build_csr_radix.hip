@@ -392,14 +392,16 @@ __global__ __launch_bounds__(kThreads, 2) void radix_pass_kernel(PassArgs a) {
     s_start[tid * DPT + j] = start[j];
   }
 
-  // Look-back for each of this thread's digits.  Two levels: tiles form groups
-  // of kGroup consecutive tickets.  A tile sums the aggregates of the earlier
-  // tiles of its group; the group's last tile publishes the group's
-  // aggregate, and later its inclusive prefix; every tile then walks back over
-  // the earlier groups' words, adding aggregates until an inclusive prefix
-  // (group 0's always is one).  Each walk reads kLookback words per digit and
-  // round, the digits' walks side by side.  Every wait is for a lower ticket,
-  // and an empty poll counts towards a bounded limit.
+  // Look-back for each of this thread's digits.  4096-key tiles, two levels:
+  // tiles form groups of kGroup consecutive tickets; a tile sums the
+  // aggregates of the earlier tiles of its group; the group's last tile
+  // publishes the group's aggregate, and later its inclusive prefix; every
+  // tile then walks back over the earlier groups' words, adding aggregates
+  // until an inclusive prefix (group 0's always is one).  7168-key tiles, one
+  // level: a walk back over the earlier tiles (tile 0's word is an inclusive
+  // prefix), then the tile's own inclusive prefix.  Each walk reads kLookback
+  // words per digit and round, the digits' walks side by side.  Every wait is
+  // for a lower ticket, and an empty poll counts towards a bounded limit.
   int spins = 0;
   // adds st[pos .. lo] (stopping early at an inclusive prefix) to sum
   auto walk = [&](const uint64_t* st, int64_t pos0, int64_t lo, uint32_t* sum) {
