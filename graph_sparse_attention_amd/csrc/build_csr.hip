@@ -35,6 +35,7 @@ struct CsrWs {
   int32_t* counts;        // [n]
   uint64_t* tile_status;  // [scan_tiles(n)]
   uint64_t* keys;         // [nnz]
+  uint64_t* tmp;          // [nnz] merge buffer of the sort of long rows
   int64_t clear_ints;     // flags + counts + tile_status, cleared in one launch
 };
 
@@ -51,6 +52,8 @@ CsrWs carve(void* ws, int32_t n, int64_t nnz) {
   p += align256(sizeof(uint64_t) * scan_tiles(n));
   w.clear_ints = (p - (uint8_t*)ws) / 4;
   w.keys = (uint64_t*)p;
+  p += align256(sizeof(uint64_t) * std::max<int64_t>(nnz, 1));
+  w.tmp = (uint64_t*)p;
   return w;
 }
 
@@ -130,6 +133,52 @@ __device__ void lds_bitonic(uint64_t* s, int P) {
   }
 }
 
+// Elements of A among the first k of the merge of sorted A [la] and B [lb]
+// (distinct keys): the merge-path co-rank, by binary search.
+__device__ __forceinline__ int co_rank(const uint64_t* A, int la, const uint64_t* B, int lb, int k) {
+  int lo = max(0, k - lb), hi = min(k, la);
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (A[mid] < B[k - mid - 1]) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// out[0 .. la + lb) = merge of sorted A and B, by the whole workgroup: output
+// tiles of kRowCap keys, whose A and B parts are staged in LDS, each thread
+// then merging kRowCap / 256 consecutive outputs of the tile from LDS.  The
+// co-ranks at the tile boundaries are found in parallel, one per thread, for
+// batches of up to 256 tiles (s_co holds 257).
+__device__ void merge_runs(const uint64_t* A, int la, const uint64_t* B, int lb, uint64_t* out, uint64_t* s,
+                           int32_t* s_co) {
+  const int total = la + lb;
+  constexpr int kPer = kRowCap / 256;
+  const int tiles = (total + kRowCap - 1) / kRowCap;
+  for (int t0 = 0; t0 < tiles; t0 += 256) {
+    const int nt = min(256, tiles - t0);
+    for (int b = threadIdx.x; b <= nt; b += blockDim.x)
+      s_co[b] = co_rank(A, la, B, lb, (int)min<int64_t>((int64_t)(t0 + b) * kRowCap, total));
+    __syncthreads();
+    for (int tt = 0; tt < nt; ++tt) {
+      const int o0 = (t0 + tt) * kRowCap, o1 = min(o0 + kRowCap, total);
+      const int i0 = s_co[tt], i1 = s_co[tt + 1];
+      const int na = i1 - i0, nb = (o1 - o0) - na;
+      for (int i = threadIdx.x; i < na; i += blockDim.x) s[i] = A[i0 + i];
+      for (int i = threadIdx.x; i < nb; i += blockDim.x) s[na + i] = B[(o0 - i0) + i];
+      __syncthreads();
+      const int k0 = min((int)threadIdx.x * kPer, o1 - o0), k1 = min(k0 + kPer, o1 - o0);
+      if (k0 < k1) {
+        int ia = co_rank(s, na, s + na, nb, k0), ib = k0 - ia;
+        for (int k = k0; k < k1; ++k) {
+          const bool take_a = ib >= nb || (ia < na && s[ia] < s[na + ib]);
+          out[o0 + k] = take_a ? s[ia++] : s[na + ib++];
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // A workgroup sorts groups of 16 destinations (grid-stride).  Each wave takes four: side by side in
 // 16-lane segments when all have <= 16 in-edges, else one after the other
 // across the wave (<= 64).  Longer rows are listed in LDS and sorted by the
@@ -145,11 +194,12 @@ __device__ __forceinline__ void row_range(const int32_t* row_ptr, int64_t r, int
 }
 
 __global__ __launch_bounds__(256) void sort_rows_kernel(int32_t n, int32_t nnz, const int32_t* __restrict__ row_ptr,
-                                                        uint64_t* __restrict__ keys, int32_t* __restrict__ col_idx,
-                                                        int32_t* __restrict__ edge_perm,
+                                                        uint64_t* __restrict__ keys, uint64_t* __restrict__ tmp,
+                                                        int32_t* __restrict__ col_idx, int32_t* __restrict__ edge_perm,
                                                         const int32_t* __restrict__ run_flag) {
   if (run_flag && *run_flag == 0) return;  // rows already in order (radix build, sorted sources)
   __shared__ uint64_t s[kRowCap];
+  __shared__ int32_t s_co[257];
   __shared__ int32_t s_long[16];
   __shared__ int32_t s_nlong;
   const int lane = threadIdx.x & 63;
@@ -215,22 +265,21 @@ __global__ __launch_bounds__(256) void sort_rows_kernel(int32_t n, int32_t nnz, 
         __syncthreads();
       }
       if (nchunks > 1) {
-        // rank of a key = its index in its own sorted chunk + keys below it in the others
-        for (int i = threadIdx.x; i < d; i += blockDim.x) {
-          const uint64_t key = keys[st + i];
-          const int own = i / kRowCap;
-          int rank = i - own * kRowCap;
-          for (int c = 0; c < nchunks; ++c) {
-            if (c == own) continue;
-            int lo = c * kRowCap, hi = min(lo + kRowCap, d);
-            while (lo < hi) {
-              const int mid = (lo + hi) >> 1;
-              if (keys[st + mid] < key) lo = mid + 1; else hi = mid;
-            }
-            rank += lo - c * kRowCap;
+        // bottom-up merges of the sorted chunks, runs R -> 2R, between the
+        // keys and the temporary array, each pair merged in output tiles of
+        // kRowCap keys staged in LDS (keys are distinct, so every merge is exact)
+        uint64_t* from = keys + st;
+        uint64_t* to = tmp + st;
+        for (int R = kRowCap; R < d; R *= 2) {
+          for (int a0 = 0; a0 < d; a0 += 2 * R) {
+            const int a1 = min(a0 + R, d), b1 = min(a0 + 2 * R, d);
+            merge_runs(from + a0, a1 - a0, from + a1, b1 - a1, to + a0, s, s_co);
           }
-          emit(col_idx, edge_perm, st + rank, key);
+          uint64_t* t = from;
+          from = to;
+          to = t;
         }
+        for (int i = threadIdx.x; i < d; i += blockDim.x) emit(col_idx, edge_perm, st + i, from[i]);
         __syncthreads();
       }
     }
@@ -240,11 +289,11 @@ __global__ __launch_bounds__(256) void sort_rows_kernel(int32_t n, int32_t nnz, 
 
 }  // namespace
 
-hipError_t launch_sort_rows(int32_t n, int64_t nnz, const int32_t* row_ptr, uint64_t* keys, int32_t* col_idx, int32_t* edge_perm,
-                            const int32_t* run_flag, hipStream_t s) {
+hipError_t launch_sort_rows(int32_t n, int64_t nnz, const int32_t* row_ptr, uint64_t* keys, uint64_t* tmp,
+                            int32_t* col_idx, int32_t* edge_perm, const int32_t* run_flag, hipStream_t s) {
   if (n > 0)
     hipLaunchKernelGGL(sort_rows_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(n, 16), 8192)), dim3(256), 0, s, n, (int32_t)nnz, row_ptr, keys,
-                       col_idx, edge_perm, run_flag);
+                       tmp, col_idx, edge_perm, run_flag);
   return hipGetLastError();
 }
 
@@ -262,7 +311,7 @@ bool csr_use_radix(int32_t n, int64_t nnz) {
 size_t build_csr_workspace_bytes(int32_t n, int64_t nnz) {
   if (csr_use_radix(n, nnz)) return build_csr_radix_workspace_bytes(n, nnz);
   return 256 + align256(sizeof(int32_t) * std::max<int64_t>(n, 1)) + align256(sizeof(uint64_t) * scan_tiles(n)) +
-         align256(sizeof(uint64_t) * std::max<int64_t>(nnz, 1));
+         2 * align256(sizeof(uint64_t) * std::max<int64_t>(nnz, 1));
 }
 
 hipError_t launch_build_csr(int32_t n, int64_t nnz, const int32_t* src, const int32_t* dst, int32_t* row_ptr,
@@ -280,7 +329,7 @@ hipError_t launch_build_csr(int32_t n, int64_t nnz, const int32_t* src, const in
   if (err != hipSuccess) return err;
   if (nnz > 0 && n > 0) {
     hipLaunchKernelGGL(scatter_kernel, dim3(eblocks), dim3(256), 0, s, src, dst, nnz, n, row_ptr, w.counts, w.keys);
-    return launch_sort_rows(n, nnz, row_ptr, w.keys, col_idx, edge_perm, nullptr, s);
+    return launch_sort_rows(n, nnz, row_ptr, w.keys, w.tmp, col_idx, edge_perm, nullptr, s);
   }
   return hipGetLastError();
 }

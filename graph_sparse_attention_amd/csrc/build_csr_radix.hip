@@ -641,7 +641,7 @@ hipError_t launch_build_csr_radix(int32_t n, int64_t nnz, const int32_t* src, co
   const unsigned rblocks = (unsigned)std::min<int64_t>(ceil_div(nnz + 1, 256 * 8), 4096);
   hipLaunchKernelGGL(radix_rowptr_kernel, dim3(rblocks), dim3(256), 0, s, w.keys[cur], nnz, n, row_ptr);
   // rows need sorting by source only when the sources were not non-decreasing
-  return launch_sort_rows(n, nnz, row_ptr, w.vals[cur], col_idx, edge_perm, &w.flags[kUnsorted], s);
+  return launch_sort_rows(n, nnz, row_ptr, w.vals[cur], w.vals[cur ^ 1], col_idx, edge_perm, &w.flags[kUnsorted], s);
 }
 
 }  // namespace gattn

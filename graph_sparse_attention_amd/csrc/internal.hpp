@@ -35,8 +35,8 @@ hipError_t launch_build_csr_radix(int32_t n, int64_t nnz, const int32_t* src, co
                                   void* ws, int32_t* status_dev, hipStream_t s);
 // sort each row's 64-bit (source << 32 | edge id) keys into col_idx / edge_perm;
 // run_flag (nullable): the launch does nothing when *run_flag == 0
-hipError_t launch_sort_rows(int32_t n, int64_t nnz, const int32_t* row_ptr, uint64_t* keys, int32_t* col_idx, int32_t* edge_perm,
-                            const int32_t* run_flag, hipStream_t s);
+hipError_t launch_sort_rows(int32_t n, int64_t nnz, const int32_t* row_ptr, uint64_t* keys, uint64_t* tmp,
+                            int32_t* col_idx, int32_t* edge_perm, const int32_t* run_flag, hipStream_t s);
 
 // Row windows -----------------------------------------------------------------
 size_t rowwindows_workspace_bytes(int32_t n, int64_t nnz);

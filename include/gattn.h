@@ -110,7 +110,7 @@ GATTN_API const char* gattn_status_string(gattn_status s);
  *   edge_perm   [nnz] int32 out, nullable: edge id of each CSR position (use it
  *               to bring per-edge tensors such as E into CSR order).
  *   workspace   device scratch of at least gattn_build_csr_workspace() bytes,
- *               256-byte aligned (about 8 bytes per edge below 2^18 edges, 25
+ *               256-byte aligned (about 16 bytes per edge below 2^18 edges, 25
  *               above, where a radix sort replaces per-edge atomics; the two
  *               builds give the same bits; GATTN_CSR_PATH=atomic|radix in the
  *               environment forces one of them, for tests and measurement, and

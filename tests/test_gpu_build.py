@@ -181,6 +181,44 @@ def test_csr_radix_many_groups(gsa, monkeypatch):
     assert_csr_equal(gsa, n, src, dst)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_csr_radix_random_sizes(gsa, seed, monkeypatch):
+    # random node counts (1 to 2^22: one to three passes of 7- to 9-bit
+    # digits) and edge counts (1 to 1.5M: one tile to many look-back groups),
+    # uniform or skewed destinations, source-sorted or shuffled
+    monkeypatch.setenv("GATTN_CSR_PATH", "radix")
+    g = np.random.default_rng(1000 + seed)
+    n = int(g.integers(1, 1 << int(g.integers(1, 23)) + 1))
+    m = int(g.integers(1, 1500000))
+    if seed % 3 == 0:
+        dst = g.integers(0, n, m)
+    else:
+        dst = np.minimum(g.zipf(1.3 + 0.2 * (seed % 4), m) - 1, n - 1) * 7919 % n
+    src = g.integers(0, n, m)
+    if seed % 2 == 0:
+        order = np.argsort(src, kind="stable")
+        src, dst = src[order], dst[order]
+    src, dst = src.astype(np.int32), dst.astype(np.int32)
+    print(f"csr radix random n={n} m={m}", flush=True)
+    assert_csr_equal(gsa, n, src, dst)
+
+
+@pytest.mark.parametrize("path,m", [("atomic", 262143), ("radix", 600000)])
+def test_csr_giant_unsorted_row(gsa, path, m, monkeypatch):
+    # one destination with every edge, sources in random order: the row is
+    # sorted as LDS-sorted chunks merged pairwise (128 / 293 chunks), a few
+    # other rows around it
+    monkeypatch.setenv("GATTN_CSR_PATH", path)
+    g = np.random.default_rng(31)
+    n = 5000
+    src = g.integers(0, n, m).astype(np.int32)
+    dst = np.full(m, 4242, np.int32)
+    dst[: m // 50] = g.integers(0, n, m // 50)
+    perm = g.permutation(m)
+    print(f"csr giant unsorted row {path} m={m}", flush=True)
+    assert_csr_equal(gsa, n, src[perm], dst[perm])
+
+
 def test_csr_empty_and_bad(gsa, csr_path):
     for n in (0, 5):
         rp, ci, pe = gpu_csr(gsa, n, np.zeros(0, np.int32), np.zeros(0, np.int32))
