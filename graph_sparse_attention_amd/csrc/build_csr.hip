@@ -13,9 +13,11 @@
 // edge id), each destination counting its in-degree back down for positions
 // -> sort every destination's keys (bitonic across the lanes of one wave, four
 // 16-key rows per wave when they fit; rows above 64 keys by the workgroup in
-// LDS, as 2048-key chunks ranked by binary search beyond that).
+// LDS, beyond 2048 keys as LDS-sorted chunks merged pairwise through a second
+// buffer).
 #include "common.hpp"
 #include "internal.hpp"
+#include "merge_runs.hpp"
 
 #include <stdlib.h>
 #include <string.h>
@@ -25,6 +27,7 @@ namespace gattn {
 namespace {
 
 constexpr int kRowCap = 2048;  // keys per LDS sort (16 KiB)
+static_assert(kRowCap == kMergeTile, "the LDS sort buffer stages the merge tiles");
 constexpr int64_t kRadixMinEdges = 1 << 18;
 
 // flag words at the head of the workspace
@@ -133,57 +136,12 @@ __device__ void lds_bitonic(uint64_t* s, int P) {
   }
 }
 
-// Elements of A among the first k of the merge of sorted A [la] and B [lb]
-// (distinct keys): the merge-path co-rank, by binary search.
-__device__ __forceinline__ int co_rank(const uint64_t* A, int la, const uint64_t* B, int lb, int k) {
-  int lo = max(0, k - lb), hi = min(k, la);
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (A[mid] < B[k - mid - 1]) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-
-// out[0 .. la + lb) = merge of sorted A and B, by the whole workgroup: output
-// tiles of kRowCap keys, whose A and B parts are staged in LDS, each thread
-// then merging kRowCap / 256 consecutive outputs of the tile from LDS.  The
-// co-ranks at the tile boundaries are found in parallel, one per thread, for
-// batches of up to 256 tiles (s_co holds 257).
-__device__ void merge_runs(const uint64_t* A, int la, const uint64_t* B, int lb, uint64_t* out, uint64_t* s,
-                           int32_t* s_co) {
-  const int total = la + lb;
-  constexpr int kPer = kRowCap / 256;
-  const int tiles = (total + kRowCap - 1) / kRowCap;
-  for (int t0 = 0; t0 < tiles; t0 += 256) {
-    const int nt = min(256, tiles - t0);
-    for (int b = threadIdx.x; b <= nt; b += blockDim.x)
-      s_co[b] = co_rank(A, la, B, lb, (int)min<int64_t>((int64_t)(t0 + b) * kRowCap, total));
-    __syncthreads();
-    for (int tt = 0; tt < nt; ++tt) {
-      const int o0 = (t0 + tt) * kRowCap, o1 = min(o0 + kRowCap, total);
-      const int i0 = s_co[tt], i1 = s_co[tt + 1];
-      const int na = i1 - i0, nb = (o1 - o0) - na;
-      for (int i = threadIdx.x; i < na; i += blockDim.x) s[i] = A[i0 + i];
-      for (int i = threadIdx.x; i < nb; i += blockDim.x) s[na + i] = B[(o0 - i0) + i];
-      __syncthreads();
-      const int k0 = min((int)threadIdx.x * kPer, o1 - o0), k1 = min(k0 + kPer, o1 - o0);
-      if (k0 < k1) {
-        int ia = co_rank(s, na, s + na, nb, k0), ib = k0 - ia;
-        for (int k = k0; k < k1; ++k) {
-          const bool take_a = ib >= nb || (ia < na && s[ia] < s[na + ib]);
-          out[o0 + k] = take_a ? s[ia++] : s[na + ib++];
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
 // A workgroup sorts groups of 16 destinations (grid-stride).  Each wave takes four: side by side in
 // 16-lane segments when all have <= 16 in-edges, else one after the other
 // across the wave (<= 64).  Longer rows are listed in LDS and sorted by the
 // whole workgroup afterwards: in LDS up to kRowCap keys, beyond that as
-// LDS-sorted chunks written back and ranked against each other.
+// LDS-sorted chunks written back and merged pairwise (runs of kRowCap,
+// 2 kRowCap, ...) between the key array and `tmp`.
 // a row's [start, start + degree) clamped to [0, nnz): a damaged row_ptr cannot
 // send a read or write outside the key and output arrays
 __device__ __forceinline__ void row_range(const int32_t* row_ptr, int64_t r, int32_t nnz, int32_t& st, int32_t& d) {
@@ -199,7 +157,7 @@ __global__ __launch_bounds__(256) void sort_rows_kernel(int32_t n, int32_t nnz, 
                                                         const int32_t* __restrict__ run_flag) {
   if (run_flag && *run_flag == 0) return;  // rows already in order (radix build, sorted sources)
   __shared__ uint64_t s[kRowCap];
-  __shared__ int32_t s_co[257];
+  __shared__ int32_t s_co[kMergeThreads + 1];
   __shared__ int32_t s_long[16];
   __shared__ int32_t s_nlong;
   const int lane = threadIdx.x & 63;
@@ -265,21 +223,9 @@ __global__ __launch_bounds__(256) void sort_rows_kernel(int32_t n, int32_t nnz, 
         __syncthreads();
       }
       if (nchunks > 1) {
-        // bottom-up merges of the sorted chunks, runs R -> 2R, between the
-        // keys and the temporary array, each pair merged in output tiles of
-        // kRowCap keys staged in LDS (keys are distinct, so every merge is exact)
-        uint64_t* from = keys + st;
-        uint64_t* to = tmp + st;
-        for (int R = kRowCap; R < d; R *= 2) {
-          for (int a0 = 0; a0 < d; a0 += 2 * R) {
-            const int a1 = min(a0 + R, d), b1 = min(a0 + 2 * R, d);
-            merge_runs(from + a0, a1 - a0, from + a1, b1 - a1, to + a0, s, s_co);
-          }
-          uint64_t* t = from;
-          from = to;
-          to = t;
-        }
-        for (int i = threadIdx.x; i < d; i += blockDim.x) emit(col_idx, edge_perm, st + i, from[i]);
+        // pairwise merges of the sorted chunks between the keys and tmp
+        const uint64_t* sorted = merge_sorted_runs(keys + st, tmp + st, d, kRowCap, s, s_co);
+        for (int i = threadIdx.x; i < d; i += blockDim.x) emit(col_idx, edge_perm, st + i, sorted[i]);
         __syncthreads();
       }
     }

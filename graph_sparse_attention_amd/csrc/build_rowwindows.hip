@@ -14,11 +14,12 @@
 // once and leaves the sorted keys in the workspace for the fill pass.  Windows up to 2048 edges
 // sort in registers (bitonic: shuffles, in-thread swaps, three rounds through
 // 16 KiB of LDS, so several windows share a CU); longer ones sort 2048-key
-// chunks that way and rank the chunks against each other by binary search in
-// the workspace.  The output does not depend on the order of the
+// chunks that way and merge them pairwise (stable merges through both key
+// arrays of the workspace).  The output does not depend on the order of the
 // sources inside a CSR row.
 #include "common.hpp"
 #include "internal.hpp"
+#include "merge_runs.hpp"
 
 namespace gattn {
 
@@ -27,6 +28,7 @@ namespace {
 constexpr int kCap = 2048;      // keys per LDS sort
 constexpr int kMaskCap = 2048;  // padded columns whose masks are assembled in LDS
 constexpr int kThreads = 256;
+static_assert(kCap == kMergeTile && kThreads == kMergeThreads, "merge tiles staged in the sort buffer");
 constexpr int kSpanBits = 4096; // a window whose sources span fewer values takes the bitmap
 constexpr int kSpanWords = kSpanBits / 32;
 
@@ -268,6 +270,7 @@ __device__ void sort_window_chunk(int32_t n, const int32_t* __restrict__ col_idx
 __global__ __launch_bounds__(kThreads) void rw_count_kernel(int32_t n, int64_t nnz, const int32_t* __restrict__ row_ptr,
                                                             const int32_t* __restrict__ col_idx, RwWs ws) {
   __shared__ uint64_t s_keys[kCap];  // sort keys, or the bitmaps of a narrow window
+  __shared__ int32_t s_co[kMergeThreads + 1];
   __shared__ int32_t s_rp[17];
   __shared__ int32_t s_wave[kThreads / 64];
   __shared__ int32_t s_red[2 * (kThreads / 64)];
@@ -312,24 +315,14 @@ __global__ __launch_bounds__(kThreads) void rw_count_kernel(int32_t n, int64_t n
         for (int i = threadIdx.x; i < cl; i += kThreads) a[cs + i] = s_keys[i];
         __syncthreads();
       }
-      // rank = index inside own chunk + keys below it in other chunks (ties: the
-      // lower chunk counts first, so equal keys still land on distinct ranks)
-      for (int i = threadIdx.x; i < len; i += kThreads) {
-        const uint64_t key = a[i];
-        const int own = i / kCap;
-        int rank = i - own * kCap;
-        for (int c = 0; c < nchunks; ++c) {
-          if (c == own) continue;
-          int lo = c * kCap, hi = min(lo + kCap, len);
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (c < own ? a[mid] <= key : a[mid] < key) lo = mid + 1; else hi = mid;
-          }
-          rank += lo - c * kCap;
-        }
-        b[rank] = key;
+      // pairwise stable merges of the sorted chunks between the two key
+      // arrays (equal keys, i.e. repeated edges, stay adjacent); the result
+      // must end in keys_b
+      const uint64_t* sorted = merge_sorted_runs(a, b, len, kCap, s_keys, s_co);
+      if (sorted != b) {
+        for (int i = threadIdx.x; i < len; i += kThreads) b[i] = sorted[i];
+        __syncthreads();
       }
-      __syncthreads();
     }
     // distinct sources and repeated keys, from the sorted keys: LDS when they
     // fit, else the workspace (two loops, so that no generic pointer can point

@@ -318,6 +318,30 @@ def test_rowwindows_long_window(gsa):
     assert_rw_equal(gsa, n, rp, ci)
 
 
+def test_rowwindows_giant_window(gsa):
+    # 16 rows x 5000 edges in one window: 40 sorted chunks merged over six
+    # levels, with sources shared between rows (duplicates across rows) and
+    # each row's sources in random order
+    n = 200000
+    g = np.random.default_rng(21)
+    pool = g.choice(n, 30000, replace=False)
+    srcs, dsts = [], []
+    for r in range(32, 48):
+        srcs.append(g.choice(pool, 5000, replace=False))
+        dsts.append(np.full(5000, r))
+    srcs.append(g.choice(n, 300, replace=False))
+    dsts.append(np.full(300, 5))
+    src, dst = np.concatenate(srcs).astype(np.int32), np.concatenate(dsts).astype(np.int32)
+    rp, ci, _ = oracle.build_csr(n, src, dst)
+    ci2 = ci.copy()
+    for i in range(32, 48):
+        g.shuffle(ci2[rp[i]:rp[i + 1]])
+    ref = oracle.rowwindows(n, rp, ci)
+    got = gpu_rw(gsa, n, rp, ci2)
+    for name, a, b in zip(("win_col_ptr", "win_cols", "tile_mask"), got, ref):
+        assert np.array_equal(a, b.reshape(a.shape)), f"{name} differs"
+
+
 @pytest.mark.parametrize("n", [40, 50000])
 def test_rowwindows_errors(gsa, n):
     # n = 40: every window's sources span < 4096 values (bitmap path); n = 50000:
