@@ -219,6 +219,19 @@ def test_csr_giant_unsorted_row(gsa, path, m, monkeypatch):
     assert_csr_equal(gsa, n, src[perm], dst[perm])
 
 
+@pytest.mark.parametrize("n", [16383, 16384, 16385, 40000])
+def test_csr_atomic_scan_sizes(gsa, n, monkeypatch):
+    # the look-back scan of the degree counts (2048 per tile): one count short
+    # of 8 full tiles, exactly 8, a 9th tile holding one count, 20 tiles
+    monkeypatch.setenv("GATTN_CSR_PATH", "atomic")
+    g = np.random.default_rng(n)
+    m = 60000
+    src = g.integers(0, n, m).astype(np.int32)
+    dst = g.integers(0, n, m).astype(np.int32)
+    dst[:50] = n - 1
+    assert_csr_equal(gsa, n, src, dst)
+
+
 def test_csr_empty_and_bad(gsa, csr_path):
     for n in (0, 5):
         rp, ci, pe = gpu_csr(gsa, n, np.zeros(0, np.int32), np.zeros(0, np.int32))
@@ -340,6 +353,19 @@ def test_rowwindows_giant_window(gsa):
     got = gpu_rw(gsa, n, rp, ci2)
     for name, a, b in zip(("win_col_ptr", "win_cols", "tile_mask"), got, ref):
         assert np.array_equal(a, b.reshape(a.shape)), f"{name} differs"
+
+
+@pytest.mark.parametrize("n", [16 * 16384 - 1, 16 * 16384, 16 * 16384 + 1])
+def test_rowwindows_scan_sizes(gsa, n):
+    # 16384 windows (8 full look-back scan tiles of window sizes, the last
+    # window full or one row short) and 16385 (a 9th tile with one window)
+    g = np.random.default_rng(n)
+    m = 50000
+    src = g.integers(0, n, m).astype(np.int32)
+    dst = g.integers(0, n, m).astype(np.int32)
+    dst[:20] = n - 1
+    rp, ci, _ = oracle.build_csr(n, src, dst)
+    assert_rw_equal(gsa, n, rp, ci)
 
 
 @pytest.mark.parametrize("n", [40, 50000])
