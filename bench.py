@@ -27,7 +27,7 @@ of the forward kernel against 8 TB/s HBM, the CPU oracle's rate on the host).
     aggregate  gattn_aggregate: V summed with seeded fp32 weights per edge and
                head, normalized by the summed weights + eps (no logits)
 
-Counter mode (used under rocprofv3 --pmc):
+Counter mode (used under rocprofv3 --pmc, one counter per run):
     python bench.py --counters-run        one copy kernel of known size, then
                                           forward launches, no timing
     python bench.py --ingest-counters DIR summarise rocprofv3 CSVs into
@@ -274,8 +274,8 @@ def ingest_counters(dirname, config, path_key, variant="forward", partition="nod
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); this build has no multi-GPU path. "
-              "How the work would shard over several GPUs is described in DESIGN.md.", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the library has no multi-GPU path; "
+              "each GPU would build and run the graphs of its own share of the batch.", file=sys.stderr)
         sys.exit(2)
     import workloads as W
     if args.ingest_counters:
