@@ -66,9 +66,9 @@ __device__ inline uint64_t* merge_sorted_runs(uint64_t* data, uint64_t* tmp, int
                                               int32_t* s_co) {
   uint64_t* from = data;
   uint64_t* to = tmp;
-  for (int R = run; R < len; R *= 2) {
-    for (int a0 = 0; a0 < len; a0 += 2 * R) {
-      const int a1 = min(a0 + R, len), b1 = min(a0 + 2 * R, len);
+  for (int64_t R = run; R < len; R *= 2) {  // 64-bit: rows of up to 2^31 - 1 keys double R past 2^30
+    for (int64_t a0 = 0; a0 < len; a0 += 2 * R) {
+      const int a1 = (int)min(a0 + R, (int64_t)len), b1 = (int)min(a0 + 2 * R, (int64_t)len);
       merge_runs(from + a0, a1 - a0, from + a1, b1 - a1, to + a0, s, s_co);
     }
     uint64_t* t = from;
