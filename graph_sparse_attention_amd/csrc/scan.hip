@@ -119,8 +119,10 @@ hipError_t launch_scan(const int32_t* in, int32_t* out, int64_t n, int32_t* bloc
 // launch order, so every tile a workgroup waits for has already started and
 // finishes without waiting on later ones.  A tile publishes its aggregate,
 // then its inclusive prefix, as one 64-bit word (flag << 32 | value).  The
-// wait is bounded: after kSpinLimit empty polls the tile reports an error
-// instead of spinning on.
+// first wave reads the words of up to 64 earlier tiles per poll and adds the
+// values up to the nearest inclusive prefix, polling again while any word in
+// that range is still empty.  The wait is bounded: after kSpinLimit such
+// polls the tile reports an error instead of spinning on.
 // ---------------------------------------------------------------------------
 namespace {
 constexpr uint32_t kFlagAggregate = 1, kFlagPrefix = 2;
@@ -151,32 +153,43 @@ __global__ __launch_bounds__(kScanThreads) void scan_lookback_kernel(const int32
   }
   int32_t total;
   const int32_t incl = block_incl_scan(s, s_wave, &total);
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {  // the first wave walks back over up to 64 earlier tiles per poll
+    const int lane = threadIdx.x;
     int32_t prefix = 0;
     if (tile == 0) {
-      publish(&tile_status[0], kFlagPrefix, total);
+      if (lane == 0) publish(&tile_status[0], kFlagPrefix, total);
     } else {
-      publish(&tile_status[tile], kFlagAggregate, total);
-      int64_t j = tile - 1;
+      if (lane == 0) publish(&tile_status[tile], kFlagAggregate, total);
+      int64_t j = tile - 1;  // lane l reads tile j - l
       int spins = 0;
-      while (j >= 0) {
-        const uint64_t w = __hip_atomic_load(&tile_status[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      while (true) {
+        const int64_t t = j - lane;
+        const uint64_t w = t >= 0 ? __hip_atomic_load(&tile_status[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                  : (uint64_t)kFlagPrefix << 32;
         const uint32_t flag = (uint32_t)(w >> 32);
-        if (flag == 0) {
+        const uint64_t pmask = __ballot(flag == kFlagPrefix), zmask = __ballot(flag == 0);
+        const int first_p = pmask ? __ffsll((unsigned long long)pmask) - 1 : 64;  // nearest inclusive prefix
+        const uint64_t need = first_p >= 63 ? ~0ull : (2ull << first_p) - 1;        // lanes 0 .. first_p
+        if (zmask & need) {  // a tile up to that prefix has not published yet
           if (++spins > kSpinLimit) {
-            err[0] = 1;
-            if (status_dev) *status_dev = GATTN_ERR_HIP;
+            if (lane == 0) {
+              err[0] = 1;
+              if (status_dev) *status_dev = GATTN_ERR_HIP;
+            }
             break;
           }
           continue;
         }
-        prefix += (int32_t)(uint32_t)w;
-        if (flag == kFlagPrefix) break;
-        --j;
+        int32_t agg = lane <= first_p ? (int32_t)(uint32_t)w : 0;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) agg += __shfl_xor(agg, o, 64);
+        prefix += agg;
+        if (first_p < 64) break;
+        j -= 64;
       }
-      publish(&tile_status[tile], kFlagPrefix, prefix + total);
+      if (lane == 0) publish(&tile_status[tile], kFlagPrefix, prefix + total);
     }
-    s_prefix = prefix;
+    if (lane == 0) s_prefix = prefix;
   }
   __syncthreads();
   int32_t run = s_prefix + incl - s;

@@ -219,10 +219,11 @@ def test_csr_giant_unsorted_row(gsa, path, m, monkeypatch):
     assert_csr_equal(gsa, n, src[perm], dst[perm])
 
 
-@pytest.mark.parametrize("n", [16383, 16384, 16385, 40000])
+@pytest.mark.parametrize("n", [16383, 16384, 16385, 40000, 131073, 300000])
 def test_csr_atomic_scan_sizes(gsa, n, monkeypatch):
     # the look-back scan of the degree counts (2048 per tile): one count short
-    # of 8 full tiles, exactly 8, a 9th tile holding one count, 20 tiles
+    # of 8 full tiles, exactly 8, a 9th tile holding one count, 20 tiles, and
+    # 65 / 147 tiles (look-backs over more than the 64 tiles one poll reads)
     monkeypatch.setenv("GATTN_CSR_PATH", "atomic")
     g = np.random.default_rng(n)
     m = 60000
