@@ -146,10 +146,24 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
-    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+def _i32(t: torch.Tensor, name: str, device=None, numel=None) -> torch.Tensor:
+    """A contiguous int32 GPU tensor, on `device` and of `numel` elements when
+    given: the kernels read every index array over its full nominal length,
+    so a short or misplaced one is refused here, before any launch."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous int32 tensor on the GPU")
+    if device is not None and t.device != torch.device(device):
+        raise ValueError(f"{name} is on {t.device}, the other tensors on {device}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
     return t
+
+
+def _csr(row_ptr, col_idx, num_nodes: int, device):
+    """row_ptr [num_nodes + 1] and col_idx [nnz], int32, on `device`."""
+    row_ptr = _i32(row_ptr, "row_ptr", device, num_nodes + 1)
+    col_idx = _i32(col_idx, "col_idx", device)
+    return row_ptr, col_idx
 
 
 def gattn_build_csr(src: torch.Tensor, dst: torch.Tensor, num_nodes: int, validate: bool = True):
@@ -157,11 +171,10 @@ def gattn_build_csr(src: torch.Tensor, dst: torch.Tensor, num_nodes: int, valida
     canonical order (destination, source, edge id).  validate=True checks
     indices and synchronizes; False keeps the call asynchronous (bad indices
     then give an unspecified CSR)."""
-    src, dst = _i32(src, "src"), _i32(dst, "dst")
+    src = _i32(src, "src")
     dev = src.device
     nnz = src.numel()
-    if dst.numel() != nnz:
-        raise ValueError("src and dst differ in length")
+    dst = _i32(dst, "dst", dev, nnz)
     nbytes = ctypes.c_size_t()
     _check(_lib.gattn_build_csr_workspace(num_nodes, nnz, ctypes.byref(nbytes)), "gattn_build_csr_workspace")
     ws = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
@@ -190,6 +203,8 @@ class CsrBuilder:
         self.status = torch.empty(1, dtype=torch.int32, device=device)
 
     def __call__(self, src: torch.Tensor, dst: torch.Tensor):
+        src = _i32(src, "src", self.row_ptr.device, self.nnz)
+        dst = _i32(dst, "dst", self.row_ptr.device, self.nnz)
         _check(_lib.gattn_build_csr(self.num_nodes, self.nnz, _ptr(src), _ptr(dst), _ptr(self.row_ptr),
                                     _ptr(self.col_idx), _ptr(self.edge_perm), _ptr(self.ws), self.ws_bytes,
                                     _ptr(self.status), _stream(src.device)), "gattn_build_csr")
@@ -219,8 +234,8 @@ class RowWindows:
 
 def gattn_build_rowwindows(row_ptr: torch.Tensor, col_idx: torch.Tensor, num_nodes: int) -> RowWindows:
     """16-row windows with 16x16 masked tiles (two calls of the C ABI)."""
-    row_ptr, col_idx = _i32(row_ptr, "row_ptr"), _i32(col_idx, "col_idx")
-    dev = row_ptr.device
+    dev = row_ptr.device if isinstance(row_ptr, torch.Tensor) else None
+    row_ptr, col_idx = _csr(row_ptr, col_idx, num_nodes, dev)
     nnz = col_idx.numel()
     nbytes = ctypes.c_size_t()
     _check(_lib.gattn_build_rowwindows_workspace(num_nodes, nnz, ctypes.byref(nbytes)),
@@ -261,10 +276,12 @@ def gattn_build_hybrid(row_ptr: torch.Tensor, col_idx: torch.Tensor, rw: RowWind
     min_density go to the MFMA path, the other rows to the gather path, in
     ranges sized like its workgroups.  q gives the geometry (N, H, D, dtype);
     the plan is for the standard mode without an edge tensor."""
-    row_ptr, col_idx = _i32(row_ptr, "row_ptr"), _i32(col_idx, "col_idx")
     if q.dim() != 3 or not q.is_cuda or q.dtype not in _DTYPES:
         raise ValueError("q must be an [N, H, D] GPU tensor")
     N = q.shape[0]
+    row_ptr, col_idx = _csr(row_ptr, col_idx, N, q.device)
+    if rw.num_nodes != N or rw.win_col_ptr.device != q.device:
+        raise ValueError("rw must be the row windows of this graph, on q's device")
     W = (N + 15) // 16
     dev = q.device
     dense = torch.empty(max(W, 1), dtype=torch.int32, device=dev)
@@ -372,24 +389,29 @@ def gattn_forward(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch.Tensor,
     workgroups: for graphs whose hubs hold many times a workgroup's share).
     hybrid (with rw): a gattn_build_hybrid plan for path "hybrid" (or
     "auto"): dense row windows on the MFMA path, the other rows gathered."""
-    row_ptr, col_idx = _i32(row_ptr, "row_ptr"), _i32(col_idx, "col_idx")
-    if q.dim() != 3 or not q.is_contiguous() or not q.is_cuda:
+    if q.dim() != 3 or not q.is_contiguous() or not q.is_cuda or q.dtype not in _DTYPES:
         raise ValueError("q must be a contiguous [N, H, D] GPU tensor")
     _check_node_tensor(k, "k", q)
     _check_node_tensor(v, "v", q)
     N, H, D = q.shape
-    if e is not None and (e.dtype != q.dtype or tuple(e.shape) != (col_idx.numel(), H, D) or not e.is_contiguous()):
-        raise ValueError("e must be a contiguous [nnz, H, D] tensor of q's dtype")
+    row_ptr, col_idx = _csr(row_ptr, col_idx, N, q.device)
+    if e is not None and (e.dtype != q.dtype or tuple(e.shape) != (col_idx.numel(), H, D) or not e.is_contiguous()
+                          or e.device != q.device):
+        raise ValueError("e must be a contiguous [nnz, H, D] tensor of q's dtype on q's device")
     if edge_ids is not None:
-        edge_ids = _i32(edge_ids, "edge_ids")
-        if edge_ids.numel() != col_idx.numel():
-            raise ValueError("edge_ids must have one entry per edge")
+        edge_ids = _i32(edge_ids, "edge_ids", q.device, col_idx.numel())
     want_e_out = e_out is not None and e_out is not False
     if e_out is True:
         e_out = torch.empty((col_idx.numel(), H, D), dtype=q.dtype, device=q.device)
     elif want_e_out and (e_out.dtype != q.dtype or tuple(e_out.shape) != (col_idx.numel(), H, D)
-                         or not e_out.is_contiguous()):
-        raise ValueError("e_out must be a contiguous [nnz, H, D] tensor of q's dtype")
+                         or not e_out.is_contiguous() or e_out.device != q.device):
+        raise ValueError("e_out must be a contiguous [nnz, H, D] tensor of q's dtype on q's device")
+    for name, x in (("rw", rw), ("hybrid", hybrid)):
+        t = None if x is None else (x.win_col_ptr if name == "rw" else x.dense_windows)
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    if rw is not None and rw.num_nodes != N:
+        raise ValueError(f"rw was built for {rw.num_nodes} nodes, q has {N}")
     if out is None:
         out = torch.empty_like(q)
     else:
@@ -418,17 +440,15 @@ def gattn_aggregate(row_ptr: torch.Tensor, col_idx: torch.Tensor, x: torch.Tenso
     """Weighted aggregation over the CSR: x [N, H, D], w [nnz, H] fp32 (row
     edge_ids[p] for position p when given); out[i] = sum_p w x[src], divided
     by (sum_p w + eps) when normalize.  workspace as in gattn_forward."""
-    row_ptr, col_idx = _i32(row_ptr, "row_ptr"), _i32(col_idx, "col_idx")
     if x.dim() != 3 or not x.is_contiguous() or not x.is_cuda or x.dtype not in _DTYPES:
         raise ValueError("x must be a contiguous [N, H, D] GPU tensor")
     N, H, D = x.shape
+    row_ptr, col_idx = _csr(row_ptr, col_idx, N, x.device)
     nnz = col_idx.numel()
     if w.dtype != torch.float32 or tuple(w.shape) != (nnz, H) or not w.is_contiguous() or w.device != x.device:
         raise ValueError("w must be a contiguous fp32 [nnz, H] tensor on x's device")
     if edge_ids is not None:
-        edge_ids = _i32(edge_ids, "edge_ids")
-        if edge_ids.numel() != nnz:
-            raise ValueError("edge_ids must have one entry per edge")
+        edge_ids = _i32(edge_ids, "edge_ids", x.device, nnz)
     if out is None:
         out = torch.empty_like(x)
     else:
@@ -449,6 +469,7 @@ def gattn_aggregate(row_ptr: torch.Tensor, col_idx: torch.Tensor, x: torch.Tenso
     return out
 
 
-__all__ = ["gattn_build_csr", "gattn_build_rowwindows", "gattn_build_hybrid", "gattn_forward", "gattn_forward_path", "gattn_aggregate",
+__all__ = ["gattn_build_csr", "gattn_build_rowwindows", "gattn_build_hybrid", "gattn_forward", "gattn_forward_path",
+           "gattn_aggregate",
            "gattn_forward_workspace", "gattn_aggregate_workspace",
            "gattn_status_string", "gattn_abi_version", "CsrBuilder", "RowWindows", "Hybrid", "GattnError", "LIB_PATH"]

@@ -1,6 +1,6 @@
 // api.cpp -- the C ABI of libgattn: argument checks, path choice, launches.
 // Every argument error is detected here, before anything is enqueued.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cstdint>
@@ -28,6 +28,17 @@ gattn_status from_hip(hipError_t e) { return e == hipSuccess ? GATTN_OK : GATTN_
 
 size_t elem_size(gattn_dtype t) { return t == GATTN_F32 ? 4 : 2; }
 
+// The integer a C caller stored in an enum field.  Loading an enum object
+// whose value lies outside the enum's range is undefined in C++, so every
+// enum that crosses the ABI is validated through its bits.
+template <typename E>
+int32_t raw_enum(const E& e) {
+  static_assert(sizeof(E) == sizeof(int32_t), "ABI enums are 32-bit");
+  int32_t v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 bool overlap(const void* a, size_t an, const void* b, size_t bn) {
   if (!a || !b || an == 0 || bn == 0) return false;
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
@@ -37,11 +48,10 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
 gattn_status check_forward(const gattn_forward_args* a, bool launch) {
   if (!a || a->struct_size != sizeof(gattn_forward_args)) return GATTN_ERR_INVALID_VALUE;
   if (a->num_nodes < 0 || a->num_heads < 1 || a->nnz < 0 || a->nnz > INT32_MAX) return GATTN_ERR_INVALID_VALUE;
-  if (a->dtype != GATTN_F32 && a->dtype != GATTN_F16 && a->dtype != GATTN_BF16) return GATTN_ERR_INVALID_VALUE;
-  if (a->mode != GATTN_SOFTMAX_STANDARD && a->mode != GATTN_SOFTMAX_CLIPPED) return GATTN_ERR_INVALID_VALUE;
-  if (a->path != GATTN_PATH_AUTO && a->path != GATTN_PATH_GATHER && a->path != GATTN_PATH_MFMA &&
-      a->path != GATTN_PATH_HYBRID)
+  if (raw_enum(a->dtype) < GATTN_F32 || raw_enum(a->dtype) > GATTN_BF16) return GATTN_ERR_INVALID_VALUE;
+  if (raw_enum(a->mode) < GATTN_SOFTMAX_STANDARD || raw_enum(a->mode) > GATTN_SOFTMAX_CLIPPED)
     return GATTN_ERR_INVALID_VALUE;
+  if (raw_enum(a->path) < GATTN_PATH_AUTO || raw_enum(a->path) > GATTN_PATH_HYBRID) return GATTN_ERR_INVALID_VALUE;
   if (a->flags & ~GATTN_FLAG_VALIDATE) return GATTN_ERR_INVALID_VALUE;
   if (!(a->scale > 0.f) || !(a->scale < INFINITY)) return GATTN_ERR_INVALID_VALUE;
   if (a->mode == GATTN_SOFTMAX_CLIPPED) {
@@ -88,7 +98,7 @@ gattn_status check_forward(const gattn_forward_args* a, bool launch) {
 gattn_status check_aggregate(const gattn_aggregate_args* a, bool launch) {
   if (!a || a->struct_size != sizeof(gattn_aggregate_args)) return GATTN_ERR_INVALID_VALUE;
   if (a->num_nodes < 0 || a->num_heads < 1 || a->nnz < 0 || a->nnz > INT32_MAX) return GATTN_ERR_INVALID_VALUE;
-  if (a->dtype != GATTN_F32 && a->dtype != GATTN_F16 && a->dtype != GATTN_BF16) return GATTN_ERR_INVALID_VALUE;
+  if (raw_enum(a->dtype) < GATTN_F32 || raw_enum(a->dtype) > GATTN_BF16) return GATTN_ERR_INVALID_VALUE;
   if (a->normalize != 0 && a->normalize != 1) return GATTN_ERR_INVALID_VALUE;
   if (!(a->eps >= 0.f) || !(a->eps < INFINITY)) return GATTN_ERR_INVALID_VALUE;
   if (a->flags & ~GATTN_FLAG_VALIDATE) return GATTN_ERR_INVALID_VALUE;
@@ -123,7 +133,7 @@ gattn_status check_aggregate(const gattn_aggregate_args* a, bool launch) {
 gattn_status check_rw(const gattn_forward_args* a) {
   const gattn_rowwindows* rw = a->rw;
   if (!rw) return GATTN_ERR_INVALID_VALUE;
-  if (rw->num_windows != (a->num_nodes + 15) / 16 || rw->num_cols < 0 || rw->num_cols % 16) return GATTN_ERR_INVALID_VALUE;
+  if ((int64_t)rw->num_windows != ((int64_t)a->num_nodes + 15) / 16 || rw->num_cols < 0 || rw->num_cols % 16) return GATTN_ERR_INVALID_VALUE;
   if (!rw->win_col_ptr || (rw->num_cols > 0 && (!rw->win_cols || !rw->tile_mask))) return GATTN_ERR_INVALID_VALUE;
   if (!aligned(rw->win_col_ptr, 4) || !aligned(rw->win_cols, 4) || !aligned(rw->tile_mask, 4))
     return GATTN_ERR_INVALID_VALUE;
@@ -135,7 +145,7 @@ gattn_status check_rw(const gattn_forward_args* a) {
 gattn_status check_hybrid(const gattn_forward_args* a) {
   const gattn_hybrid* hy = a->hybrid;
   if (!hy) return GATTN_ERR_INVALID_VALUE;
-  const int32_t W = (a->num_nodes + 15) / 16;
+  const int32_t W = (int32_t)(((int64_t)a->num_nodes + 15) / 16);
   if (hy->num_dense < 0 || hy->num_dense > W || hy->num_ranges < 0 || hy->num_ranges > a->num_nodes)
     return GATTN_ERR_INVALID_VALUE;
   if ((hy->num_dense > 0 && !hy->dense_windows) || (hy->num_ranges > 0 && !hy->ranges)) return GATTN_ERR_INVALID_VALUE;
@@ -204,8 +214,8 @@ extern "C" {
 
 int gattn_abi_version(void) { return GATTN_ABI_VERSION; }
 
-const char* gattn_status_string(gattn_status s) {
-  switch (s) {
+const char* gattn_status_string(gattn_status status) {
+  switch (raw_enum(status)) {
     case GATTN_OK: return "ok";
     case GATTN_ERR_INVALID_VALUE: return "invalid argument";
     case GATTN_ERR_UNSUPPORTED: return "unsupported configuration";
@@ -266,7 +276,7 @@ gattn_status gattn_build_rowwindows(int32_t num_nodes, int64_t nnz, const int32_
         !aligned(tile_mask, 4))
       return GATTN_ERR_INVALID_VALUE;
     if (workspace_bytes < rowwindows_workspace_bytes(num_nodes, nnz)) return GATTN_ERR_BUFFER_TOO_SMALL;
-    const int64_t W = (num_nodes + 15) / 16;
+    const int64_t W = ((int64_t)num_nodes + 15) / 16;
     // win_col_ptr is int32: its total, at most nnz + 15 W, must fit
     if (nnz + 15 * W > INT32_MAX) return GATTN_ERR_UNSUPPORTED;
     if (!win_cols) {
@@ -311,7 +321,7 @@ gattn_status gattn_build_hybrid(const gattn_forward_args* args, float min_densit
     if (!mfma_supported(*args)) return GATTN_ERR_UNSUPPORTED;
     if ((st = check_rw(args)) != GATTN_OK) return st;
     if (!(min_density >= 0.f) || !(min_density < INFINITY)) return GATTN_ERR_INVALID_VALUE;
-    const int32_t n = args->num_nodes, W = (n + 15) / 16;
+    const int32_t n = args->num_nodes, W = (int32_t)(((int64_t)n + 15) / 16);
     if (n > 0 && (!dense_windows || !ranges)) return GATTN_ERR_INVALID_VALUE;
     if (!aligned(dense_windows, 4) || !aligned(ranges, 4)) return GATTN_ERR_INVALID_VALUE;
     *plan = gattn_hybrid{0, 0, 1, dense_windows, ranges};

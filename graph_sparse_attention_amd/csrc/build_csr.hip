@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void sort_rows_kernel(int32_t n, int32_t nnz, 
   __shared__ int32_t s_long[16];
   __shared__ int32_t s_nlong;
   const int lane = threadIdx.x & 63;
-  const int64_t groups = (n + 15) / 16;
+  const int64_t groups = ((int64_t)n + 15) / 16;
   for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
     if (threadIdx.x == 0) s_nlong = 0;
     __syncthreads();

@@ -43,10 +43,13 @@
 //    boundaries (edge-parallel parts, Fused3S Figure 2's node- vs edge-parallel
 //    split).  Each part leaves its (m, l, acc) in the workspace and raises a
 //    flag tagged with this launch's token; a part that then finds every flag of
-//    the row raised merges the parts in order and writes the row.  Several
-//    parts may merge; they write identical bits.  No counter needs clearing,
-//    and no cache flush is needed: the parts and flags are written and read
-//    with device-coherent (agent-scope) accesses, each wait ordering them.
+//    the row raised merges the parts in order, writes the row and lowers the
+//    row's flags again.  Several parts may merge; they write identical bits.
+//    The random token guards against whatever a new workspace holds; lowering
+//    the flags makes a repeated token (a HIP graph replays its launch
+//    arguments) safe.  No cache flush is needed: the parts and flags are
+//    written and read with device-coherent (agent-scope) accesses, each wait
+//    ordering them.
 #pragma once
 
 #include <algorithm>
@@ -676,6 +679,15 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
           M::fold(mm, ll, aa, ld(a.ws_ml + qb * 2), ld(a.ws_ml + qb * 2 + 1), a2);
         }
         if (active) M::store(a, a.out + (row * rowstride + eoff) * ESZ, ll, aa);
+        // Lower the row's flags again.  Every flag a launch raises is back at
+        // 0 when it ends, so a launch whose token repeats (a captured launch
+        // replayed from a HIP graph keeps its arguments) never finds an
+        // earlier launch's flags raised and never merges its stale parts.  A
+        // part still reading the flags then sees a 0 and leaves the merge to
+        // this one.
+        for (int64_t bb = b0 + lig; bb <= b1; bb += G)
+          __hip_atomic_store(a.ws_flags + part(bb == b0 ? 1 : 0, bb), (uint64_t)0, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }

@@ -1,7 +1,7 @@
 // internal.hpp -- host-side launchers shared between api.cpp and the kernels.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 

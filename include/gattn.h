@@ -222,9 +222,11 @@ typedef struct {
      whose partial softmax states are merged in order (Fused3S Figure 2's
      node- versus edge-parallel split).  Without it, workgroups take equal
      numbers of destinations.  Size from gattn_forward_workspace; 256-byte
-     aligned; any contents on entry (flags are tagged per call); must not
-     alias any other argument; one workspace must not serve two calls that
-     run at the same time.  Ignored on the MFMA path.                           */
+     aligned; any contents on entry (flags are tagged with a random per-call
+     token, and every flag a call raises is lowered again before it ends, so
+     a call captured in a HIP graph may be replayed); must not alias any
+     other argument; one workspace must not serve two calls that run at the
+     same time.  Ignored on the MFMA path.                                      */
   void* workspace;
   size_t workspace_bytes;
   /* Per-window plan for the HYBRID path: [host] struct of device arrays built

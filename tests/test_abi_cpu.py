@@ -310,3 +310,4 @@ def test_workspace_query_errors(gsa):
     # nothing to compute: no workspace, no HIP call
     a = fake_args(gsa, num_nodes=0, nnz=0)
     assert L.gattn_forward_workspace(ctypes.byref(a), ctypes.byref(nb)) == gsa.GATTN_OK and nb.value == 0
+

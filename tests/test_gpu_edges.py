@@ -3,9 +3,9 @@ the RTMScore edge update (e_out), the edge-id indirection of per-edge rows,
 and weighted aggregation with given per-edge weights (gattn_aggregate).
 
 Tolerances are those of the forward (tests/parity.py): fp32 componentwise
-against the oracle's magnitude of the same sum, fp16 / bf16 relative L2.
-The edge update is one product per element, so its fp32 bound is relative
-to the element itself."""
+against the oracle's magnitude of the same sum, fp16 / bf16 relative L2 plus
+the per-element bound.  The edge update is one product per element, so its
+bounds are relative to the element itself."""
 import math
 
 import numpy as np
@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import FP32_TOL, REL_L2_TOL, case, check_forward, componentwise, rel_l2
+from parity import FP32_TOL, REL_L2_TOL, case, check_forward, componentwise, half_elementwise, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -34,6 +34,8 @@ def check_edges(y_gpu, ref, dtype):
     else:
         err = rel_l2(y, ref)
         assert err <= REL_L2_TOL[dtype], f"{dtype} edge-update rel-L2 {err:.3e} > {REL_L2_TOL[dtype]}"
+        elem = half_elementwise(y, ref, np.abs(ref), dtype)
+        assert elem <= 1.0, f"{dtype} edge-update element error {elem:.3f} of its bound"
     return err
 
 

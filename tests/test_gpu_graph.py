@@ -74,3 +74,51 @@ def test_graph_replays_match_eager(gsa, cfg, path, ws):
         for name, got, want in zip(("row_ptr", "col_idx", "edge_perm"), (b.row_ptr, b.col_idx, b.edge_perm), ref_csr):
             assert torch.equal(got, want), f"replay {i}: {name} differs"
         assert torch.equal(out, ref), f"replay {i}: forward output differs"
+
+
+@pytest.mark.parametrize("mode", ["standard", "clipped"])
+def test_graph_replays_with_new_inputs_balanced(gsa, mode):
+    # The balanced partition cuts config 3's hub rows (up to 2000 in-edges)
+    # across workgroups and merges their parts through the workspace.  One
+    # workspace serves the captured launch, whose token the graph keeps;
+    # q, k, v change before every replay, eager launches on the same
+    # workspace run in between, and each replay must equal an eager launch on
+    # the same inputs with a workspace of its own.
+    c = case(3)
+    wl = c.wl
+    print(f"graph replay with new inputs, config 3 balanced, {mode}", flush=True)
+    rp, ci = torch.from_numpy(c.rp).cuda(), torch.from_numpy(c.ci).cuda()
+    deg = torch.diff(rp)
+    q, k, v = c.q.clone(), c.k.clone(), c.v.clone()
+    ws = torch.empty(gsa.gattn_forward_workspace(rp, ci, q, k, v, mode=mode), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5)                       # arbitrary contents on entry
+
+    def step(workspace, out=None):
+        return gsa.gattn_forward(rp, ci, q, k, v, mode=mode, scale=wl.scale, path="gather", workspace=workspace,
+                                 out=out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = step(ws)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    hubs = torch.nonzero(deg > 500).flatten()
+    assert hubs.numel() > 0
+    for i in range(4):
+        for t in (q, k, v):
+            t.copy_(torch.randn(t.shape, generator=gen, device="cuda").to(t.dtype))
+        want = step(True)
+        if i % 2:
+            step(ws)                     # eager work on the captured launch's workspace
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out[hubs], want[hubs]), f"replay {i}: hub rows differ from the eager launch"
+        assert torch.equal(out, want), f"replay {i}: output differs from the eager launch"

@@ -106,6 +106,28 @@ def test_dense_bruteforce(orc, n, h, d, mode, with_e, seed, self_loops):
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("mode", ["standard", "clipped"])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_magnitude_is_weighted_abs_sum(orc, mode, seed):
+    """S = sum_p alpha_p |v_p|, the scale that the fp32 and half-precision
+    tolerances are measured against, equals the dense brute force run on |V|
+    (independent code, same weights) and, bit for bit, the oracle's own
+    output with V replaced by |V| (same weights, same summation order)."""
+    n = [9, 23, 37][seed]
+    src, dst = W.random_graph(960, seed, n, 12)
+    q, k, v, e = feats(seed, n, src.shape[0], 2, 8, True)
+    q *= 2.0
+    out, mag = run_oracle(orc, n, src, dst, q, k, v, e, mode, 0.3, want_mag=True)
+    ref = dense_bruteforce(n, src, dst, q, k, np.abs(v), e, mode, 0.3, -5.0, 5.0, 1e-6)
+    np.testing.assert_allclose(mag, ref, rtol=0, atol=1e-12)
+    assert np.array_equal(mag, run_oracle(orc, n, src, dst, q, k, np.abs(v), e, mode, 0.3))
+    assert np.all(mag >= np.abs(out) - 1e-12)
+    # a row subset returns the same magnitudes
+    rows = np.arange(n - 1, -1, -2, dtype=np.int32)
+    _, mag_rows = run_oracle(orc, n, src, dst, q, k, v, e, mode, 0.3, want_mag=True, rows=rows)
+    assert np.array_equal(mag_rows, mag[rows])
+
+
 @settings(max_examples=40, deadline=None)
 @given(n=st.integers(1, 30), h=st.sampled_from([1, 2]), d=st.sampled_from([4, 8]),
        mode=st.sampled_from(["standard", "clipped"]), with_e=st.booleans(), seed=st.integers(0, 10_000))

@@ -53,6 +53,9 @@ MUTANTS = {
         "return (x < y) - (x > y);\n}\nstatic int cmp_i32"),
     "csr_edge_id_tiebreak_reversed": (
         "| (uint64_t)(uint32_t)e;", "| (uint64_t)(uint32_t)(0x7fffffff - e);"),
+    "magnitude_without_weight": (
+        "if (mg) mg[c] += a * fabs(vj[c]);", "if (mg) mg[c] += fabs(vj[c]);"),
+    "magnitude_signed": ("if (mg) mg[c] += a * fabs(vj[c]);", "if (mg) mg[c] += a * vj[c];"),
     "window_padding_zero": ("t < u ? buf[t] : -1;", "t < u ? buf[t] : 0;"),
     "window_mask_transposed": (
         "tile_mask[tile * 16 + (r - r0)] |= (uint16_t)(1u << (t % 16));",
@@ -79,6 +82,7 @@ def battery(orc):
         tfwd.test_aggregate_matches_scipy(orc, normalize, True)
     tfwd.test_aggregate_closed_form(orc)
     for mode in ("standard", "clipped"):
+        tfwd.test_magnitude_is_weighted_abs_sum(orc, mode, 0)
         tfwd.test_weights_sum(orc, mode)
         tfwd.test_invariants(orc, mode)
     for seed in range(4):
