@@ -9,6 +9,7 @@ current stream.  Names follow the C ABI in ``include/gattn.h``:
     gattn_forward(row_ptr, col_idx, q, k, v, ...)   -> out [N, H, D]  (, e_out)
     gattn_build_hybrid(row_ptr, col_idx, rw, q)     -> Hybrid (per-window plan)
     gattn_forward_path(...)                         -> "gather" | "mfma" | "hybrid"
+    gattn_forward_noalloc(row_ptr, col_idx, q, k, v, out, ...) -> out (no allocation)
     gattn_aggregate(row_ptr, col_idx, x, w, ...)    -> out [N, H, D]
 
 Every call raises if ``libgattn.so`` is missing or stale: there is no
@@ -34,6 +35,7 @@ GATTN_F32, GATTN_F16, GATTN_BF16 = range(3)
 GATTN_SOFTMAX_STANDARD, GATTN_SOFTMAX_CLIPPED = range(2)
 GATTN_PATH_AUTO, GATTN_PATH_GATHER, GATTN_PATH_MFMA, GATTN_PATH_HYBRID = range(4)
 GATTN_FLAG_VALIDATE = 1
+GATTN_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _DTYPES = {torch.float32: GATTN_F32, torch.float16: GATTN_F16, torch.bfloat16: GATTN_BF16}
 _MODES = {"standard": GATTN_SOFTMAX_STANDARD, "clipped": GATTN_SOFTMAX_CLIPPED}
@@ -108,13 +110,14 @@ def _load():
                                          ctypes.c_size_t, vp]
     L.gattn_forward.argtypes = [ctypes.POINTER(_ForwardArgs), vp]
     L.gattn_forward_path.argtypes = [ctypes.POINTER(_ForwardArgs), ctypes.POINTER(ctypes.c_int)]
+    L.gattn_forward_noalloc.argtypes = [ctypes.POINTER(_ForwardArgs), vp]
     L.gattn_aggregate.argtypes = [ctypes.POINTER(_AggregateArgs), vp]
     L.gattn_forward_workspace.argtypes = [ctypes.POINTER(_ForwardArgs), sz]
     L.gattn_build_hybrid.argtypes = [ctypes.POINTER(_ForwardArgs), ctypes.c_float, vp, vp, ctypes.POINTER(_Hybrid), vp]
     L.gattn_aggregate_workspace.argtypes = [ctypes.POINTER(_AggregateArgs), sz]
     for f in (L.gattn_build_csr_workspace, L.gattn_build_csr, L.gattn_build_rowwindows_workspace,
               L.gattn_build_rowwindows, L.gattn_forward, L.gattn_forward_path, L.gattn_aggregate,
-              L.gattn_forward_workspace, L.gattn_aggregate_workspace, L.gattn_build_hybrid):
+              L.gattn_forward_workspace, L.gattn_aggregate_workspace, L.gattn_build_hybrid, L.gattn_forward_noalloc):
         f.restype = st
     return L
 
@@ -424,6 +427,41 @@ def gattn_forward(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch.Tensor,
     return (out, e_out) if want_e_out else out
 
 
+def gattn_forward_noalloc(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                          v: torch.Tensor, out: torch.Tensor, e: Optional[torch.Tensor] = None,
+                          mode: str = "standard", scale: Optional[float] = None, clip=(-5.0, 5.0),
+                          eps: float = 1e-6, path: str = "auto", rw: Optional[RowWindows] = None,
+                          edge_ids: Optional[torch.Tensor] = None, e_out: Optional[torch.Tensor] = None,
+                          hybrid: Optional[Hybrid] = None) -> torch.Tensor:
+    """gattn_forward for callers that cannot allocate: the gather path runs
+    the balanced partition with its workspace in the library's fixed scratch
+    array (GATTN_NOALLOC_SCRATCH_BYTES per GPU).  `out` (and `e_out`, when
+    wanted) must be given; nothing is allocated here or in the library.
+    Calls whose executions overlap on one GPU race on the scratch array."""
+    if out is None:
+        raise ValueError("gattn_forward_noalloc writes into a given `out`")
+    if q.dim() != 3 or not q.is_contiguous() or not q.is_cuda or q.dtype not in _DTYPES:
+        raise ValueError("q must be a contiguous [N, H, D] GPU tensor")
+    for name, t in (("k", k), ("v", v), ("out", out)):
+        _check_node_tensor(t, name, q)
+    N, H, D = q.shape
+    row_ptr, col_idx = _csr(row_ptr, col_idx, N, q.device)
+    nnz = col_idx.numel()
+    if e is not None and (e.dtype != q.dtype or tuple(e.shape) != (nnz, H, D) or not e.is_contiguous()
+                          or e.device != q.device):
+        raise ValueError("e must be a contiguous [nnz, H, D] tensor of q's dtype on q's device")
+    if e_out is not None and (e_out.dtype != q.dtype or tuple(e_out.shape) != (nnz, H, D)
+                              or not e_out.is_contiguous() or e_out.device != q.device):
+        raise ValueError("e_out must be a contiguous [nnz, H, D] tensor of q's dtype on q's device")
+    if edge_ids is not None:
+        edge_ids = _i32(edge_ids, "edge_ids", q.device, nnz)
+    a, keep = _forward_args(row_ptr, col_idx, q, k, v, e, out, mode, scale, clip, eps, path, rw, False,
+                            edge_ids, e_out, hybrid)
+    _check(_lib.gattn_forward_noalloc(ctypes.byref(a), _stream(q.device)), "gattn_forward_noalloc")
+    del keep
+    return out
+
+
 def gattn_forward_path(row_ptr, col_idx, q, k, v, e=None, mode="standard", path="auto",
                        rw: Optional[RowWindows] = None, hybrid: Optional[Hybrid] = None) -> str:
     a, keep = _forward_args(row_ptr, col_idx, q, k, v, e, None, mode, None, (-5.0, 5.0), 1e-6, path, rw, False,
@@ -470,6 +508,6 @@ def gattn_aggregate(row_ptr: torch.Tensor, col_idx: torch.Tensor, x: torch.Tenso
 
 
 __all__ = ["gattn_build_csr", "gattn_build_rowwindows", "gattn_build_hybrid", "gattn_forward", "gattn_forward_path",
-           "gattn_aggregate",
+           "gattn_forward_noalloc", "gattn_aggregate",
            "gattn_forward_workspace", "gattn_aggregate_workspace",
            "gattn_status_string", "gattn_abi_version", "CsrBuilder", "RowWindows", "Hybrid", "GattnError", "LIB_PATH"]

@@ -17,6 +17,7 @@ static_assert(sizeof(gattn_forward_args) == 168, "gattn_forward_args layout");
 static_assert(sizeof(gattn_hybrid) == 32, "gattn_hybrid layout");
 static_assert(sizeof(gattn_aggregate_args) == 104, "gattn_aggregate_args layout");
 static_assert(sizeof(gattn_rowwindows) == 40, "gattn_rowwindows layout");
+static_assert(kStaticScratchBytes == GATTN_NOALLOC_SCRATCH_BYTES, "scratch size of gattn_forward_noalloc");
 
 namespace {
 
@@ -428,6 +429,35 @@ gattn_status gattn_forward(const gattn_forward_args* args, hipStream_t stream) {
     if (args->workspace && args->workspace_bytes < forward_gather_workspace_bytes(*args))
       return GATTN_ERR_BUFFER_TOO_SMALL;
     return from_hip(launch_forward_gather(*args, stream));
+  } catch (...) {
+    return GATTN_ERR_HIP;
+  }
+}
+
+gattn_status gattn_forward_noalloc(const gattn_forward_args* args, hipStream_t stream) {
+  try {
+    gattn_status st = check_forward(args, true);
+    if (st != GATTN_OK) return st;
+    // the scratch is the library's; validation would copy to the host
+    if (args->workspace || args->workspace_bytes || (args->flags & GATTN_FLAG_VALIDATE))
+      return GATTN_ERR_INVALID_VALUE;
+    gattn_path path;
+    if ((st = resolve(args, &path)) != GATTN_OK) return st;
+    if (args->num_nodes == 0) return GATTN_OK;
+    if (path == GATTN_PATH_MFMA) return from_hip(launch_forward_mfma(*args, nullptr, 0, stream));
+    if (path == GATTN_PATH_HYBRID) {
+      const gattn_hybrid* hy = args->hybrid;
+      if ((st = from_hip(launch_forward_mfma(*args, hy->dense_windows, hy->num_dense, stream))) != GATTN_OK) return st;
+      return from_hip(launch_forward_gather_ranges(*args, hy->ranges, hy->num_ranges, hy->range_rows, stream));
+    }
+    const size_t need = forward_gather_workspace_bytes(*args);
+    if (need > kStaticScratchBytes) return GATTN_ERR_BUFFER_TOO_SMALL;
+    void* scratch = nullptr;
+    if (static_scratch(&scratch) != hipSuccess) return GATTN_ERR_HIP;
+    gattn_forward_args a = *args;
+    a.workspace = scratch;
+    a.workspace_bytes = kStaticScratchBytes;
+    return from_hip(launch_forward_gather(a, stream));
   } catch (...) {
     return GATTN_ERR_HIP;
   }

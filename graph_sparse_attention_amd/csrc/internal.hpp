@@ -69,6 +69,11 @@ size_t aggregate_workspace_bytes(const gattn_aggregate_args& a);
 // applicability of the MFMA row-window path (no launch)
 bool mfma_supported(const gattn_forward_args& a);
 
+// The fixed scratch array of gattn_forward_noalloc (one per GPU, alive until
+// the process ends) and its device address on the current device.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+hipError_t static_scratch(void** ptr);
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace gattn

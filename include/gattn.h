@@ -242,6 +242,31 @@ typedef struct {
  * into range so that a bad graph gives wrong numbers, never a fault.        */
 GATTN_API gattn_status gattn_forward(const gattn_forward_args* args /*[host]*/, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * gattn_forward_noalloc: gattn_forward for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  On the gather path it runs the balanced partition
+ * (as gattn_forward with a workspace, same kernels, same bits) with its
+ * workspace in a scratch array inside the library: one array of
+ * GATTN_NOALLOC_SCRATCH_BYTES per GPU, reserved when the library's code is
+ * loaded on that GPU and held until the process ends.  The MFMA and hybrid
+ * paths use no scratch and run as in gattn_forward.
+ *   args: as for gattn_forward, with workspace NULL and workspace_bytes 0
+ *         (GATTN_ERR_INVALID_VALUE otherwise) and without GATTN_FLAG_VALIDATE
+ *         (which copies to the host; GATTN_ERR_INVALID_VALUE).  The caller
+ *         still provides every input and `out`.
+ *   GATTN_ERR_BUFFER_TOO_SMALL when the problem's balanced-partition
+ *         workspace (gattn_forward_workspace) exceeds the array; use
+ *         gattn_forward with a workspace, or without one, instead.
+ * Calls no allocating routine.  Every call on one GPU uses that GPU's array,
+ * which keeps what the last call left (nothing in it needs clearing: its
+ * flags are tagged per call and lowered again before a call ends).  Two calls
+ * whose executions overlap on one GPU (different streams, or host threads)
+ * race on the array and give wrong results: order them on one stream.
+ * ------------------------------------------------------------------------ */
+#define GATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+GATTN_API gattn_status gattn_forward_noalloc(const gattn_forward_args* args /*[host]*/, hipStream_t stream);
+
 /* The path gattn_forward would take for these arguments (no work enqueued; `out` may be NULL). */
 GATTN_API gattn_status gattn_forward_path(const gattn_forward_args* args /*[host]*/, gattn_path* path /*[host]*/);
 

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(gsa):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     lib = ctypes.CDLL(gsa.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), f"{name} declared in gattn.h but not exported"
@@ -311,3 +311,31 @@ def test_workspace_query_errors(gsa):
     a = fake_args(gsa, num_nodes=0, nnz=0)
     assert L.gattn_forward_workspace(ctypes.byref(a), ctypes.byref(nb)) == gsa.GATTN_OK and nb.value == 0
 
+
+def test_noalloc_host_checks(gsa):
+    # gattn_forward_noalloc refuses, before touching a device: a caller
+    # workspace, the validating flag (a host copy), and a problem whose
+    # balanced-partition workspace exceeds the library's scratch array
+    L = gsa._lib
+    text = open(HEADER).read()
+    m = re.search(r"#define GATTN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == gsa.GATTN_NOALLOC_SCRATCH_BYTES
+    base = 1 << 32
+    a = fake_args(gsa, workspace=base + (20 << 20), workspace_bytes=4096)
+    assert L.gattn_forward_noalloc(ctypes.byref(a), None) == gsa.GATTN_ERR_INVALID_VALUE
+    a = fake_args(gsa, flags=gsa.GATTN_FLAG_VALIDATE)
+    assert L.gattn_forward_noalloc(ctypes.byref(a), None) == gsa.GATTN_ERR_INVALID_VALUE
+    a = fake_args(gsa, head_dim=40)
+    assert L.gattn_forward_noalloc(ctypes.byref(a), None) == gsa.GATTN_ERR_UNSUPPORTED
+    assert L.gattn_forward_noalloc(None, None) == gsa.GATTN_ERR_INVALID_VALUE
+    # a huge graph (tensors far apart so that none overlaps): its workspace
+    # exceeds the scratch array
+    big = fake_args(gsa, num_nodes=400_000_000, nnz=2_000_000_000, num_heads=1, head_dim=64,
+                    row_ptr=1 << 40, col_idx=2 << 40, q=3 << 40, k=4 << 40, v=5 << 40, out=6 << 40)
+    nb = ctypes.c_size_t(0)
+    assert L.gattn_forward_workspace(ctypes.byref(big), ctypes.byref(nb)) == gsa.GATTN_OK
+    assert nb.value > gsa.GATTN_NOALLOC_SCRATCH_BYTES
+    assert L.gattn_forward_noalloc(ctypes.byref(big), None) == gsa.GATTN_ERR_BUFFER_TOO_SMALL
+    # nothing to compute
+    a = fake_args(gsa, num_nodes=0, nnz=0)
+    assert L.gattn_forward_noalloc(ctypes.byref(a), None) == gsa.GATTN_OK
