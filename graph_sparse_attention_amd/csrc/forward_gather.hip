@@ -98,18 +98,25 @@ Plan make_plan(const Problem& p) {
   const double target = (double)g.geo.ns * GATTN_GATHER_EDGES_PER_SLOT * u;  // edges per workgroup
   g.npw = nodes_per_wg(p, target, qcap, g.geo.head_blocks, (int64_t)detail::resident_of<kPartNode>(p) * cus);
 
-  // balanced partition over T = N + nnz items
+  // balanced partition over T = N + nnz items: one round of resident
+  // workgroups (every workgroup then finds its range while the memory system
+  // is still idle; a second round would pay the search and staging round
+  // trips again, each several times longer under full load), more only when
+  // a workgroup's typical row count would exceed the rows whose Q it stages
   {
     const int64_t resident_split = (int64_t)detail::resident_of<kPartSplit>(p) * cus;
-    const int64_t per_round_split = std::max<int64_t>(1, resident_split / g.geo.head_blocks);
+    const int64_t per_round = std::max<int64_t>(1, resident_split / g.geo.head_blocks);
     const int64_t T = (int64_t)p.n + p.nnz;
     const int64_t cmax = kMaxNodesPerWg - 2;
-    double c0 = p.nnz > 0 ? target * (double)T / (double)p.nnz : (double)cmax;
-    c0 = std::min(c0, (double)qcap * (double)T / (double)p.n);   // typical rows per workgroup <= qcap
-    int64_t C = std::min<int64_t>(cmax, std::max<int64_t>(8, (int64_t)c0));
-    const double wgs = (double)ceil_div(T, C) * g.geo.head_blocks;
-    const int64_t rounds = std::max<int64_t>(1, (int64_t)std::llround(wgs / (double)resident_split));
-    C = std::min<int64_t>(cmax, std::max<int64_t>(8, ceil_div(T, rounds * per_round_split)));
+    const int qcap_s = p.mode == kModeAggregate
+                           ? kMaxNodesPerWg
+                           : std::max(1, std::min(kMaxNodesPerWg, kQLdsBytesSplit / g.geo.qrow));
+    const double c_rows = (double)qcap_s * (double)T / (double)p.n;   // items of a typical qcap_s rows
+    int64_t C = std::max<int64_t>(8, ceil_div(T, per_round));
+    if ((double)C > c_rows) C = std::max<int64_t>(8, (int64_t)c_rows);
+    C = std::min<int64_t>(C, cmax);
+    const int64_t rounds = ceil_div(ceil_div(T, C), per_round);
+    C = std::min<int64_t>(cmax, std::max<int64_t>(8, ceil_div(T, rounds * per_round)));
     g.C = C;
     g.B = ceil_div(T, C);
     g.light_max = (int)std::max<int64_t>(2, C / 2);

@@ -38,7 +38,8 @@
 //    one batched graph, whose sources are nearby, share an L2.
 //  * With a workspace, workgroups instead take equal ranges of the merged
 //    sequence of row ends and edges (a merge path over the whole CSR), found
-//    by a 64-lane search of row_ptr at the start.  A light row belongs whole to
+//    by a 64-lane search of row_ptr at the start; one round of resident
+//    workgroups, each staging up to 24 KB of Q rows.  A light row belongs whole to
 //    the workgroup holding its first item; a heavy row is cut at the range
 //    boundaries (edge-parallel parts, Fused3S Figure 2's node- vs edge-parallel
 //    split).  Each part leaves its (m, l, acc) in the workspace and raises a
@@ -60,6 +61,9 @@
 
 #ifndef GATTN_GATHER_Q_LDS_BYTES
 #define GATTN_GATHER_Q_LDS_BYTES 12288  // Q rows staged per workgroup
+#endif
+#ifndef GATTN_GATHER_Q_LDS_BYTES_SPLIT
+#define GATTN_GATHER_Q_LDS_BYTES_SPLIT 24576  // the same for the balanced partition
 #endif
 #ifndef GATTN_GATHER_EDGES_PER_SLOT
 #define GATTN_GATHER_EDGES_PER_SLOT 3   // target edges per slot, in units of U
@@ -91,6 +95,7 @@ namespace gattn {
 constexpr int kGatherThreads = 256;
 constexpr int kMaxNodesPerWg = 1024;
 constexpr int kQLdsBytes = GATTN_GATHER_Q_LDS_BYTES;
+constexpr int kQLdsBytesSplit = GATTN_GATHER_Q_LDS_BYTES_SPLIT;
 constexpr int kModeAggregate = 2;  // given per-edge weights instead of logits and softmax
 
 // How workgroups divide the CSR (the kernel's PART parameter).
@@ -138,21 +143,47 @@ struct Cut {
 };
 
 // Start of the range that begins at item x, computed by one whole wave: r0 is
-// the last row with first_item(r0) <= x, found with a 64-position window
-// around the proportional guess (exact for uniform degrees), then a 64-way
-// search.  A light row straddling x was taken by the workgroup holding its
-// first item, so the range starts at the next row; a heavy row is cut at x.
+// the last row with first_item(r0) <= x.  Two round trips in the usual case:
+// 64 samples 128 rows apart around the proportional guess bracket r0 within
+// 128 rows (graphs whose cumulative degree stays within 4096 rows of its
+// average slope), then those 128 rows, two per lane, give r0 and, from the
+// same loads, its first and last edge.  Otherwise a 64-way search over the
+// side the samples point to.  A light row straddling x was taken by the
+// workgroup holding its first item, so the range starts at the next row; a
+// heavy row is cut at x.
 __device__ inline Cut locate(const GatherArgs& a, int64_t x, int lane) {
   const int n = a.n, nnz = (int)a.nnz;
   if (x >= a.total_items) return Cut{n, nnz, 0};
-  int64_t lo = 0, hi = n;
+  auto cut_at = [&](int r0, int rs, int re) -> Cut {
+    if (r0 + (int64_t)rs == x) return Cut{r0, rs, 0};
+    const int64_t e = x - r0;
+    if (re - rs + 1 > a.light_max && e > rs && e < re) return Cut{r0, (int)e, 1};
+    return Cut{r0 + 1, re, 0};
+  };
+  constexpr int64_t S = 128;
+  int64_t lo = 0, hi = n;  // r0 lies in [lo, hi]
   {
-    const int64_t g = min(max(x * n / a.total_items - 32, (int64_t)0), max((int64_t)n - 63, (int64_t)0));
-    const int64_t pos = min(g + lane, (int64_t)n);
-    const int k = __popcll(__ballot(first_item(a, pos) <= x));
-    if (k == 0) hi = max(g - 1, (int64_t)0);
-    else if (k == 64) lo = g + 63;
-    else lo = hi = g + k - 1;
+    const int64_t g = x * n / a.total_items;
+    const int64_t base = min(max(g - 32 * S, (int64_t)0), max((int64_t)n - 63 * S, (int64_t)0));
+    const int64_t fa = first_item(a, min(base + (int64_t)lane * S, (int64_t)n));
+    const int k = __popcll(__ballot(fa <= x));
+    if (k == 0) {
+      hi = max(base - 1, (int64_t)0);
+    } else if (k == 64) {
+      lo = base + 63 * S;
+    } else {
+      // r0 in [p, p + S); row p + S is lane k's sample (past n: first_item(n) = N + nnz > x)
+      const int64_t p = base + (int64_t)(k - 1) * S;
+      const int64_t fnext = __shfl(fa, k, 64);
+      const int64_t f0 = first_item(a, min(p + lane, (int64_t)n));
+      const int64_t f1 = first_item(a, min(p + 64 + lane, (int64_t)n));
+      const int c = __popcll(__ballot(f0 <= x)) + __popcll(__ballot(f1 <= x));  // >= 1: row p qualifies
+      const int64_t r0 = p + c - 1;
+      if (r0 >= n) return Cut{n, nnz, 0};  // only reachable for a malformed row_ptr
+      const int64_t fr = c <= 64 ? __shfl(f0, c - 1, 64) : __shfl(f1, c - 65, 64);
+      const int64_t fn = c < 64 ? __shfl(f0, c, 64) : (c < 128 ? __shfl(f1, c - 64, 64) : fnext);
+      return cut_at((int)r0, (int)(fr - r0), (int)(fn - (r0 + 1)));
+    }
   }
   while (hi > lo) {
     const int64_t step = (hi - lo + 63) / 64;
@@ -163,11 +194,7 @@ __device__ inline Cut locate(const GatherArgs& a, int64_t x, int lane) {
   }
   const int r0 = (int)lo;
   if (r0 >= n) return Cut{n, nnz, 0};
-  const int rs = min(max(a.row_ptr[r0], 0), nnz), re = min(max(a.row_ptr[r0 + 1], 0), nnz);
-  if (r0 + (int64_t)rs == x) return Cut{r0, rs, 0};
-  const int64_t e = x - r0;
-  if (re - rs + 1 > a.light_max && e > rs && e < re) return Cut{r0, (int)e, 1};
-  return Cut{r0 + 1, re, 0};
+  return cut_at(r0, min(max(a.row_ptr[r0], 0), nnz), min(max(a.row_ptr[r0 + 1], 0), nnz));
 }
 
 template <typename T, int D, int MODE, bool HAS_E, bool EOUT>
@@ -265,9 +292,10 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
   // reads by then.  Sharing that buffer keeps a workgroup's LDS at about
   // 26 KB for 16-bit types (6 workgroups per CU) instead of 37 KB (4).
   constexpr int kRec1Bytes = kGatherThreads * (VEC + 2) * (int)sizeof(float);
-  static_assert(AGG || kRec1Bytes <= kQLdsBytes, "records [1] must fit the Q staging buffer");
+  constexpr int kQLds = PART == kPartSplit ? kQLdsBytesSplit : kQLdsBytes;
+  static_assert(AGG || kRec1Bytes <= kQLds, "records [1] must fit the Q staging buffer");
   __shared__ int32_t s_rp[kMaxNodesPerWg + 1];
-  __shared__ __attribute__((aligned(16))) uint8_t s_q[AGG ? kRec1Bytes : kQLdsBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[AGG ? kRec1Bytes : kQLds];
   __shared__ float s_pm0[kGatherThreads];
   __shared__ float s_pl0[kGatherThreads];
   __shared__ float s_pacc0[kGatherThreads * VEC];
@@ -324,7 +352,7 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
       nn = min(a.npw, a.n - n0);
     }
   }
-  const int qcap = AGG ? 0 : kQLdsBytes / qrow;  // rows whose Q is staged in LDS
+  const int qcap = AGG ? 0 : kQLds / qrow;  // rows whose Q is staged in LDS
   auto rp_val = [&](int t, int v) {
     v = min(max(v, 0), nnz_i);
     if (split && t == nn) v = s_cut[4];
