@@ -9,14 +9,15 @@
 //   S^T (16 src x 16 rows) = K_t (16 x D) . Q_w^T (D x 16)
 //        v_mfma_f32_16x16x32_{f16,bf16}, D/32 steps.  Lane l holds
 //        S[row l%16][src 4(l/16)+i], i = 0..3.
-//   masked entries -> -inf; running row max / sum in fp32 (online softmax)
+//   masked entries -> -inf; running row max / sum in fp32 (online softmax),
+//        reduced over a row's four 16-lane groups with cross-row lane swaps
 //   O^T (D x 16 rows) += V_t^T (D x 16 src) . P^T (16 src x 16 rows)
 //        v_mfma_f32_16x16x16_{f16,bf16}, D/16 blocks.  The B operand P^T
 //        needs lane l to hold P[row l%16][src 4(l/16)+i] -- exactly the S^T
 //        accumulator layout, so P goes from the SDDMM accumulators to the
 //        SpMM operand without leaving the registers (our counterpart of
-//        Fused3S's register remapping).  V_t^T is read transposed from a
-//        per-wave LDS copy of the tile's V rows.
+//        Fused3S's register remapping).  V_t^T comes from a per-wave LDS
+//        copy of the tile's V rows through gfx950's transposing LDS read.
 //   O^T accumulators keep row l%16 in lane l like the softmax state, so the
 //   per-row rescale is a register multiply.
 //
@@ -45,7 +46,8 @@ struct MfmaArgs {
   const int32_t* __restrict__ windows;  // nullable: the grid's windows (a hybrid plan's dense ones)
   int64_t num_cols;
   int32_t n, H, W;
-  float scale_l2;  // scale * log2(e)
+  float scale_l2;     // scale * log2(e)
+  uint32_t kv_bytes;  // bytes of K (and of V), at most 2^31
 };
 
 template <bool BF16>
@@ -64,21 +66,57 @@ __device__ __forceinline__ f32x4 mfma_pv(uint2 a, uint2 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one row's four
+// 16-lane groups) with the cross-row swaps of gfx950: called with the same
+// value twice, each returns a lane's own value and its partner's (l ^ 32,
+// then l ^ 16), in an order that may differ between lanes; max and a
+// two-term sum do not depend on it, so all four lanes get the same result.
+__device__ __forceinline__ float rows_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+  const uint32_t v = __builtin_bit_cast(uint32_t, x);
+  auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)q[0]), __builtin_bit_cast(float, (uint32_t)q[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
+  const uint32_t v = __builtin_bit_cast(uint32_t, x);
+  auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return __builtin_bit_cast(float, (uint32_t)q[0]) + __builtin_bit_cast(float, (uint32_t)q[1]);
+}
+
 template <bool BF16>
 __device__ __forceinline__ uint16_t to_bits(float x) {
   if constexpr (BF16) return (uint16_t)bf16_rne(x);
   else return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format;
+// the range check then makes an out-of-range load return zeros without any
+// memory access).
+constexpr int32_t kBufferWord3 = 0x00020000;
+// Offset of a padding column's loads: past the end of K and V, which the host
+// keeps at or below 2^31 bytes, so no offset wraps around.
+constexpr uint32_t kPastEnd = 0x80000000u;
+
+// Two tiles in flight per wave: while tile t computes, tile t + 1's K rows
+// (registers) and V rows (LDS) are loading.  V goes straight from memory into
+// one of two per-wave LDS buffers (direct-to-LDS loads, no registers), and
+// tile t reads its V^T from its buffer into registers before tile t + 1's
+// loads are issued, so the wait that precedes that read covers only loads
+// the tile needs anyway.  K and V are addressed through buffer resources: a
+// padding column's loads fall past the end, return zeros and reach no memory.
 template <bool BF16, int D>
 // The second launch bound (at least 2 waves per SIMD) makes the compiler pack
-// the registers: 80 for D = 64 (6 waves per SIMD), 52 for D = 32, 112 for
-// D = 128, without spills; with no bound it takes 96 for D = 64.
+// the registers.
 __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
   constexpr int KS = D / 32;   // 16x16x32 steps for S^T
   constexpr int NB = D / 16;   // 16-wide d blocks for O^T
-  constexpr int LDW = D + 8;   // LDS row pitch in 16-bit elements (breaks bank aliasing)
-  __shared__ uint16_t s_v[kWavesPerWg][16 * LDW];
+  constexpr int VB = KS * 1024;  // one tile's V rows in LDS: KS loads of 64 lanes x 16 bytes
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[kWavesPerWg][2][VB];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wb = (int)xcd_contiguous_block(blockIdx.x, gridDim.x);
@@ -86,16 +124,15 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
   const int h = blockIdx.y * kWavesPerWg + wave;
   if (h >= a.H || w < 0 || w >= a.W) return;
   const int r = lane & 15, g = lane >> 4;
-  const int node = 16 * w + r;
-  const bool row_ok = node < a.n;
   const int64_t rowstride = (int64_t)a.H * D;
-  uint16_t* sv = s_v[wave];
 
   // B operand of S^T: Q_w^T, lane holds Q[row r][d = 32s + 8g .. +7]
   u32x4 qf[KS];
+  const int node = 16 * w + r;
 #pragma unroll
   for (int s = 0; s < KS; ++s)
-    qf[s] = row_ok ? ld16(a.q + (int64_t)node * rowstride + (int64_t)h * D + 32 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+    qf[s] = node < a.n ? ld16(a.q + (int64_t)node * rowstride + (int64_t)h * D + 32 * s + 8 * g)
+                       : u32x4{0u, 0u, 0u, 0u};
 
   const int64_t c0 = min<int64_t>(max(a.win_col_ptr[w], 0), a.num_cols) & ~int64_t(15);
   const int64_t c1 = min<int64_t>(max<int64_t>(a.win_col_ptr[w + 1], c0), a.num_cols) & ~int64_t(15);
@@ -103,34 +140,60 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
   float m = -INFINITY, l = 0.f;
   f32x4 o[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NB; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Loads are issued with no branch around them (a padding column reads row
-  // 0, whose V is zeroed before use).  One register set per tile: the
-  // (window, head) waves of a CU hide each other's load latency, and a second
-  // set for the next tile's rows would cost two waves per SIMD.
-  auto load_kv = [&](int32_t col, u32x4* kk, u32x4* vv) {
-    const int64_t src_off = (int64_t)((uint32_t)col < (uint32_t)a.n ? col : 0) * rowstride + (int64_t)h * D;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)a.k, (short)0, (int)a.kv_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)a.v, (short)0, (int)a.kv_bytes, kBufferWord3);
+  // lane (r, g)'s byte offset of column col's row, head h, d = 8g (per step s: + 64 s)
+  auto row_off = [&](int32_t col) -> uint32_t {
+    return (uint32_t)col < (uint32_t)a.n ? (uint32_t)(((uint64_t)col * rowstride + (uint64_t)h * D + 8 * g) * 2)
+                                         : kPastEnd;
+  };
+  // tile loads: K rows into registers, V rows into LDS buffer vb, where lane
+  // (r, g) of step s writes V[column r][d = 32s + 8g .. +7] at byte 16 (16 g + r)
+  // of the step's 1024-byte block
+  auto issue = [&](int32_t col, u32x4* kk, int vb) {
+    const uint32_t off = row_off(col);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      kk[s] = ld16(a.k + src_off + 32 * s + 8 * g);
-      vv[s] = ld16(a.v + src_off + 32 * s + 8 * g);
+    for (int s = 0; s < KS; ++s)
+      kk[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off + 64 * s, 0, 0));
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)&s_v[wave][vb][s * 1024],
+                                               16, off + 64 * s, 0, 0, 0);
+  };
+  // V^T operand of d block j: lane (i = lane % 16, q = lane / 16) takes
+  // V[source 4q + t][d = 16j + i], t = 0..3, from one transposing LDS read.
+  // That read hands lane i of each 16-lane group element i % 4 of the 8 bytes
+  // addressed by lane 4t + i / 4 of the group; so lane k of group q addresses
+  // V[source 4q + k / 4][d = 16j + 4 (k % 4) .. +3], 8 contiguous bytes of
+  // the 16 that one direct-to-LDS lane wrote.
+  auto read_vt = [&](int vb, uint2* va) {
+    // The compiler does not order these LDS reads after the direct-to-LDS
+    // loads that fill the buffer: wait for every load in flight explicitly
+    // (here they are all this tile's rows or the next tile's column ids),
+    // with compiler fences so that no read moves above the wait.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const int src = 4 * g + (r >> 2);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int d0 = 16 * j + 4 * (r & 3);
+      const int byte = (d0 >> 5) * 1024 + 16 * (16 * ((d0 & 31) >> 3) + src) + 2 * (d0 & 7);
+      va[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                            (__attribute__((address_space(3))) i16x4*)(
+                                                (__attribute__((address_space(3))) uint8_t*)&s_v[wave][vb][0] + byte)));
     }
   };
-  // tile at column c with rows (kf, vf), column id col and row mask `mask`
-  auto tile = [&](u32x4* kf, u32x4* vf, int32_t col, uint32_t mask) {
+  // one tile: S^T on the matrix cores, the online softmax over the tile's 16
+  // sources per row, P^T straight from the accumulator registers, and O^T +=
+  // V^T P^T
+  auto compute = [&](const u32x4* kf, const uint2* va, uint32_t mask) {
     const uint32_t bits = mask >> (4 * g);
-    if ((uint32_t)col >= (uint32_t)a.n) {  // padding column: no edge, V row zero
-#pragma unroll
-      for (int s = 0; s < KS; ++s) vf[s] = u32x4{0u, 0u, 0u, 0u};
-    }
-
-    // SDDMM on the matrix cores
     f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) st = mfma_qk<BF16>(kf[s], qf[s], st);
-
-    // online softmax over this tile's 16 sources, per row r
     float x[4];
     float tmax = -INFINITY;
 #pragma unroll
@@ -138,8 +201,7 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
       x[i] = (bits >> i & 1u) ? st[i] * a.scale_l2 : -INFINITY;
       tmax = fmaxf(tmax, x[i]);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = rows_max(tmax);
     const float mn = fmaxf(m, tmax);
     const float mu = mn == -INFINITY ? 0.f : mn;
     const float corr = m == mn ? 1.f : fast_exp2(m - mu);  // exp2(0) kept exact
@@ -149,56 +211,62 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
       p[i] = x[i] == mu ? 1.f : fast_exp2(x[i] - mu);
       psum += p[i];
     }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
+    psum = rows_sum(psum);
     l = l * corr + psum;
     m = mn;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) o[b] *= corr;
-
-    // P^T operand straight from the accumulator registers
     uint2 pb;
     pb.x = (uint32_t)to_bits<BF16>(p[0]) | ((uint32_t)to_bits<BF16>(p[1]) << 16);
     pb.y = (uint32_t)to_bits<BF16>(p[2]) | ((uint32_t)to_bits<BF16>(p[3]) << 16);
-
-    // V tile rows -> LDS, read back transposed as the A operand V^T
 #pragma unroll
-    for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x4*>(sv + r * LDW + 32 * s + 8 * g) = vf[s];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const uint16_t* col0 = sv + (4 * g) * LDW + 16 * b + r;
-      uint2 va;
-      va.x = (uint32_t)col0[0] | ((uint32_t)col0[LDW] << 16);
-      va.y = (uint32_t)col0[2 * LDW] | ((uint32_t)col0[3 * LDW] << 16);
-      o[b] = mfma_pv<BF16>(va, pb, o[b]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int j = 0; j < NB; ++j) o[j] = mfma_pv<BF16>(va[j], pb, o[j] * corr);
   };
+  // column c + r's id (lane r's K / V source) and the mask of row r of tile c / 16
+  auto meta = [&](int64_t c, int32_t& col, uint32_t& mask) {
+    col = a.win_cols[c + r];
+    mask = a.tile_mask[c + r];
+  };
+
   if (c0 < c1) {
-    u32x4 kf[KS], vf[KS];
-    for (int64_t c = c0; c < c1; c += 16) {
-      const int32_t col = a.win_cols[c + r];
-      const uint32_t mask = a.tile_mask[c + r];
-      load_kv(col, kf, vf);
-      tile(kf, vf, col, mask);
+    int32_t colA, colB = -1;
+    uint32_t maskA = 0, maskB = 0;
+    u32x4 kA[KS], kB[KS];
+    uint2 va[NB];
+    meta(c0, colA, maskA);
+    if (c0 + 16 < c1) meta(c0 + 16, colB, maskB);
+    issue(colA, kA, 0);
+    // tiles c (set A, buffer 0) and c + 16 (set B, buffer 1) per pass; the
+    // branches are uniform across the wave
+    for (int64_t c = c0; c < c1; c += 32) {
+      read_vt(0, va);
+      if (c + 16 < c1) issue(colB, kB, 1);
+      int32_t colA2 = -1;
+      uint32_t maskA2 = 0;
+      if (c + 32 < c1) meta(c + 32, colA2, maskA2);
+      compute(kA, va, maskA);
+      if (c + 16 >= c1) break;
+      read_vt(1, va);
+      if (c + 32 < c1) issue(colA2, kA, 0);
+      int32_t colB2 = -1;
+      uint32_t maskB2 = 0;
+      if (c + 48 < c1) meta(c + 48, colB2, maskB2);
+      compute(kB, va, maskB);
+      colA = colA2;
+      colB = colB2;
+      maskA = maskA2;
+      maskB = maskB2;
     }
   }
 
-  // O[row r][d = 16b + 4g + i] = O^T[d][r] / l  (row without edges -> 0)
-  if (row_ok) {
+  // O[row][d = 16j + 4g + i] = O^T[d][row] / l  (row without edges -> 0)
+  if (node < a.n) {
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     uint16_t* dst = a.out + (int64_t)node * rowstride + (int64_t)h * D + 4 * g;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
+    for (int j = 0; j < NB; ++j) {
       uint2 w2;
-      w2.x = (uint32_t)to_bits<BF16>(o[b][0] * inv) | ((uint32_t)to_bits<BF16>(o[b][1] * inv) << 16);
-      w2.y = (uint32_t)to_bits<BF16>(o[b][2] * inv) | ((uint32_t)to_bits<BF16>(o[b][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(dst + 16 * b) = w2;
+      w2.x = (uint32_t)to_bits<BF16>(o[j][0] * inv) | ((uint32_t)to_bits<BF16>(o[j][1] * inv) << 16);
+      w2.y = (uint32_t)to_bits<BF16>(o[j][2] * inv) | ((uint32_t)to_bits<BF16>(o[j][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(dst + 16 * j) = w2;
     }
   }
 }
@@ -218,8 +286,9 @@ hipError_t launch_b(const gattn_forward_args& fa, const MfmaArgs& ma, int32_t bl
 }  // namespace
 
 bool mfma_supported(const gattn_forward_args& a) {
+  const uint64_t kv_bytes = (uint64_t)a.num_nodes * a.num_heads * a.head_dim * 2;
   return (a.dtype == GATTN_F16 || a.dtype == GATTN_BF16) && a.mode == GATTN_SOFTMAX_STANDARD && a.e == nullptr &&
-         (a.head_dim == 32 || a.head_dim == 64 || a.head_dim == 128);
+         (a.head_dim == 32 || a.head_dim == 64 || a.head_dim == 128) && kv_bytes <= ((uint64_t)1 << 31);
 }
 
 hipError_t launch_forward_mfma(const gattn_forward_args& fa, const int32_t* windows, int32_t num_windows,
@@ -239,6 +308,7 @@ hipError_t launch_forward_mfma(const gattn_forward_args& fa, const int32_t* wind
   ma.H = fa.num_heads;
   ma.W = fa.rw->num_windows;
   ma.scale_l2 = fa.scale * kLog2e;
+  ma.kv_bytes = (uint32_t)((uint64_t)fa.num_nodes * fa.num_heads * fa.head_dim * 2);
   const int32_t blocks = windows ? num_windows : ma.W;
   return fa.dtype == GATTN_BF16 ? launch_b<true>(fa, ma, blocks, s) : launch_b<false>(fa, ma, blocks, s);
 }
