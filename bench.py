@@ -320,6 +320,18 @@ def load_traffic(path_key, config, variant="forward", partition="node"):
     return d
 
 
+def counter_commands(dirname, config, path_key, variant, partition):
+    """The runs behind a counter file: from /tmp with TMPDIR=/tmp, R = the
+    repository root, one run per counter, the CSVs under DIR/FETCH and
+    DIR/WRITE, then the ingestion from the repository root."""
+    args = (f"--config {config} --path {path_key}" + (f" --variant {variant}" if variant != "forward" else "")
+            + (" --partition balanced" if partition == "balanced" and path_key == "gather" else ""))
+    rel = os.path.relpath(os.path.abspath(dirname), ROOT)
+    return ([f"rocprofv3 --pmc {ctr} -d $R/{rel}/{ctr.split('_')[0]} -o run --output-format csv -- "
+             f"python3 -u $R/bench.py {args} --counters-run" for ctr in ("FETCH_SIZE", "WRITE_SIZE")]
+            + [f"python3 bench.py {args} --ingest-counters {rel}"])
+
+
 def ingest_counters(dirname, config, path_key, variant="forward", partition="node"):
     """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the forward kernel
     and of the calibration copy; scale by the copy's bytes-per-count."""
@@ -359,15 +371,7 @@ def ingest_counters(dirname, config, path_key, variant="forward", partition="nod
            "fetch_kib_per_dispatch": res.get("fwd_FETCH_SIZE"), "write_kib_per_dispatch": res.get("fwd_WRITE_SIZE"),
            "copy_fetch_kib": copy_read, "copy_write_kib": copy_write, "copy_bytes_each_way": COPY_BYTES,
            "read_scale": fr, "write_scale": fw,
-           "commands": [f"rocprofv3 --pmc {ctr} -d {os.path.join(dirname, ctr.split('_')[0].lower())} -o run "
-                        f"--output-format csv -- python -u bench.py --config {config} --path {path_key}"
-                        + (f" --variant {variant}" if variant != "forward" else "")
-                        + (" --partition balanced" if partition == "balanced" and path_key == "gather" else "")
-                        + " --counters-run" for ctr in ("FETCH_SIZE", "WRITE_SIZE")]
-                       + [f"python bench.py --config {config} --path {path_key}"
-                          + (f" --variant {variant}" if variant != "forward" else "")
-                          + (" --partition balanced" if partition == "balanced" and path_key == "gather" else "")
-                          + f" --ingest-counters {dirname}"]}
+           "commands": counter_commands(dirname, config, path_key, variant, partition)}
     if res.get("fwd_FETCH_SIZE") is not None and fr and res.get("fwd_WRITE_SIZE") is not None and fw:
         out["hbm_bytes_per_launch"] = res["fwd_FETCH_SIZE"] * 1024.0 * fr + res["fwd_WRITE_SIZE"] * 1024.0 * fw
     os.makedirs(PROFILES, exist_ok=True)
