@@ -34,6 +34,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWavesPerWg = 4;
+constexpr int kMetaCols = 256;  // column ids (and masks) a wave stages in LDS at a time
 
 struct MfmaArgs {
   const int32_t* __restrict__ win_col_ptr;
@@ -117,6 +118,9 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
   constexpr int NB = D / 16;   // 16-wide d blocks for O^T
   constexpr int VB = KS * 1024;  // one tile's V rows in LDS: KS loads of 64 lanes x 16 bytes
   __shared__ __attribute__((aligned(16))) uint8_t s_v[kWavesPerWg][2][VB];
+  // a wave's window: column ids and masks of up to kMetaCols / 16 tiles at a time
+  __shared__ int32_t s_col[kWavesPerWg][kMetaCols];
+  __shared__ uint32_t s_msk[kWavesPerWg][kMetaCols / 2];  // two 16-bit masks per word
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wb = (int)xcd_contiguous_block(blockIdx.x, gridDim.x);
@@ -220,35 +224,54 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) o[j] = mfma_pv<BF16>(va[j], pb, o[j] * corr);
   };
-  // column c + r's id (lane r's K / V source) and the mask of row r of tile c / 16
-  auto meta = [&](int64_t c, int32_t& col, uint32_t& mask) {
-    col = a.win_cols[c + r];
-    mask = a.tile_mask[c + r];
+  // column c + r's id (lane r's K / V source) and the mask of row r of tile
+  // c / 16, c counted from the start of the staged chunk
+  auto meta = [&](int32_t c, int32_t& col, uint32_t& mask) {
+    col = s_col[wave][c + r];
+    mask = reinterpret_cast<const uint16_t*>(s_msk[wave])[c + r];
   };
 
-  if (c0 < c1) {
+  // The window's ids and masks go to LDS once per chunk of up to 16 tiles, 64
+  // ids or 128 masks per direct-to-LDS load (lane l's 4 bytes land at 4 l),
+  // instead of two loads per tile: the kernel is bound by the rate at which a
+  // CU issues vector memory instructions, not by their bytes.
+  for (int64_t cb = c0; cb < c1; cb += kMetaCols) {
+    const int32_t n = (int32_t)min<int64_t>(kMetaCols, c1 - cb);
+    const __amdgpu_buffer_rsrc_t rc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.win_cols + cb), (short)0, n * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rm =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.tile_mask + cb), (short)0, n * 2, kBufferWord3);
+    for (int i = 0; i < n; i += 64)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (__attribute__((address_space(3))) void*)&s_col[wave][i], 4,
+                                               (uint32_t)(i + lane) * 4, 0, 0, 0);
+    for (int i = 0; i < n; i += 128)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (__attribute__((address_space(3))) void*)&s_msk[wave][i / 2], 4,
+                                               (uint32_t)(2 * i + 4 * lane), 0, 0, 0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     int32_t colA, colB = -1;
     uint32_t maskA = 0, maskB = 0;
     u32x4 kA[KS], kB[KS];
     uint2 va[NB];
-    meta(c0, colA, maskA);
-    if (c0 + 16 < c1) meta(c0 + 16, colB, maskB);
+    meta(0, colA, maskA);
+    if (16 < n) meta(16, colB, maskB);
     issue(colA, kA, 0);
-    // tiles c (set A, buffer 0) and c + 16 (set B, buffer 1) per pass; the
+    // tiles c (set A, buffer 0) and c + 16 (set B, buffer 1) of the chunk per pass; the
     // branches are uniform across the wave
-    for (int64_t c = c0; c < c1; c += 32) {
+    for (int32_t c = 0; c < n; c += 32) {
       read_vt(0, va);
-      if (c + 16 < c1) issue(colB, kB, 1);
+      if (c + 16 < n) issue(colB, kB, 1);
       int32_t colA2 = -1;
       uint32_t maskA2 = 0;
-      if (c + 32 < c1) meta(c + 32, colA2, maskA2);
+      if (c + 32 < n) meta(c + 32, colA2, maskA2);
       compute(kA, va, maskA);
-      if (c + 16 >= c1) break;
+      if (c + 16 >= n) break;
       read_vt(1, va);
-      if (c + 32 < c1) issue(colA2, kA, 0);
+      if (c + 32 < n) issue(colA2, kA, 0);
       int32_t colB2 = -1;
       uint32_t maskB2 = 0;
-      if (c + 48 < c1) meta(c + 48, colB2, maskB2);
+      if (c + 48 < n) meta(c + 48, colB2, maskB2);
       compute(kB, va, maskB);
       colA = colA2;
       colB = colB2;
