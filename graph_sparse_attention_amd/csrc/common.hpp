@@ -24,6 +24,11 @@ template <> struct Elem<_Float16> { static constexpr int kVec = 8; static conste
 template <> struct Elem<bf16_t> { static constexpr int kVec = 8; static constexpr gattn_dtype kDtype = GATTN_BF16; };
 
 // ---- 16-byte loads / stores -------------------------------------------------
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format).
+// The range check then makes each dword of a load that falls past the
+// resource's size return zero without any memory access.
+constexpr int32_t kBufferWord3 = 0x00020000;
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));

@@ -95,10 +95,6 @@ __device__ __forceinline__ uint16_t to_bits(float x) {
   else return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
-// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format;
-// the range check then makes an out-of-range load return zeros without any
-// memory access).
-constexpr int32_t kBufferWord3 = 0x00020000;
 // Offset of a padding column's loads: past the end of K and V, which the host
 // keeps at or below 2^31 bytes, so no offset wraps around.
 constexpr uint32_t kPastEnd = 0x80000000u;
