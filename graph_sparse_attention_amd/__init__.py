@@ -12,6 +12,12 @@ current stream.  Names follow the C ABI in ``include/gattn.h``:
     gattn_forward_noalloc(row_ptr, col_idx, q, k, v, out, ...) -> out (no allocation)
     gattn_aggregate(row_ptr, col_idx, x, w, ...)    -> out [N, H, D]
 
+and, on top of them, a graph object for callers that hold a COO edge list:
+
+    g = Graph.from_coo(src, dst, num_nodes)         # CSR built on the device once
+    g.rowwindows()                                  # the MFMA path's windows (built once)
+    forward(g, q, k, v, e=None, mode=..., ...)      -> out [N, H, D]  (e in COO edge order)
+
 Every call raises if ``libgattn.so`` is missing or stale: there is no
 fallback implementation.  Build it with ``python -m
 graph_sparse_attention_amd.build``.
@@ -507,7 +513,55 @@ def gattn_aggregate(row_ptr: torch.Tensor, col_idx: torch.Tensor, x: torch.Tenso
     return out
 
 
-__all__ = ["gattn_build_csr", "gattn_build_rowwindows", "gattn_build_hybrid", "gattn_forward", "gattn_forward_path",
+@dataclasses.dataclass
+class Graph:
+    """A graph as the kernels read it: CSR by destination in canonical order
+    (destination, source, edge id), plus edge_perm[p] = the original COO id
+    of the edge at CSR position p.  Built on the device by from_coo; the row
+    windows of the MFMA path are built on the first rowwindows() call and
+    kept (that build synchronizes once, for its size query)."""
+    num_nodes: int
+    row_ptr: torch.Tensor      # int32 [N + 1]
+    col_idx: torch.Tensor      # int32 [nnz]
+    edge_perm: torch.Tensor    # int32 [nnz]
+    _rw: Optional[RowWindows] = dataclasses.field(default=None, repr=False)
+
+    @classmethod
+    def from_coo(cls, src: torch.Tensor, dst: torch.Tensor, num_nodes: int, validate: bool = True) -> "Graph":
+        """Edges src[i] -> dst[i] (int32 GPU tensors); validate=True rejects
+        indices outside [0, num_nodes) (and synchronizes)."""
+        row_ptr, col_idx, edge_perm = gattn_build_csr(src, dst, num_nodes, validate)
+        return cls(num_nodes, row_ptr, col_idx, edge_perm)
+
+    @property
+    def nnz(self) -> int:
+        return self.col_idx.numel()
+
+    def rowwindows(self) -> RowWindows:
+        if self._rw is None:
+            self._rw = gattn_build_rowwindows(self.row_ptr, self.col_idx, self.num_nodes)
+        return self._rw
+
+
+def forward(graph: Graph, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, e: Optional[torch.Tensor] = None,
+            mode: str = "standard", scale: Optional[float] = None, clip=(-5.0, 5.0), eps: float = 1e-6,
+            path: str = "auto", out: Optional[torch.Tensor] = None, e_out=None, workspace=None):
+    """gattn_forward on a Graph.  e (and e_out, when asked for) are indexed
+    by the caller's original edge ids -- the COO order from_coo was given --
+    and reached through graph.edge_perm, as the gattn-triton article reaches
+    its edge tensor through the CSC edge ids.  With fp16 / bf16 inputs, the
+    standard mode and no e, paths "auto" and "mfma" use the graph's row
+    windows (built on first use); "auto" then takes the MFMA path for dense
+    windows, else the gather path."""
+    rw = None
+    if path in ("auto", "mfma") and q.dtype != torch.float32 and mode == "standard" and e is None:
+        rw = graph.rowwindows()
+    ids = graph.edge_perm if (e is not None or (e_out is not None and e_out is not False)) else None
+    return gattn_forward(graph.row_ptr, graph.col_idx, q, k, v, e, mode=mode, scale=scale, clip=clip, eps=eps,
+                         path=path, rw=rw, out=out, edge_ids=ids, e_out=e_out, workspace=workspace)
+
+
+__all__ = ["Graph", "forward", "gattn_build_csr", "gattn_build_rowwindows", "gattn_build_hybrid", "gattn_forward", "gattn_forward_path",
            "gattn_forward_noalloc", "gattn_aggregate",
            "gattn_forward_workspace", "gattn_aggregate_workspace",
            "gattn_status_string", "gattn_abi_version", "CsrBuilder", "RowWindows", "Hybrid", "GattnError", "LIB_PATH"]
