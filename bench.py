@@ -91,6 +91,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=8.0,
                    help="single-thread oracle time the CPU sample is sized for")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle (and with it the parity check)")
+    p.add_argument("--eager", action="store_true",
+                   help="also time an eager PyTorch formulation of the same forward (context only)")
     p.add_argument("--counters-run", action="store_true")
     p.add_argument("--ingest-counters", default=None)
     args = p.parse_args()
@@ -299,6 +301,61 @@ def cpu_baseline(wl, host, gpu_out, seconds, variant="forward"):
             "sample": sample, "value_1_thread": round(edges / t1 / 1e9, 6), "csr_build_s_1_thread": round(t_build, 3)}
     check = {"rows": int(rows.shape[0]), "edges": edges, "passed": bool(ok), **figures}
     return base, check
+
+
+# ---------------------------------------------------------------------------
+# eager PyTorch context
+# ---------------------------------------------------------------------------
+
+def eager_forward(torch, dst, src, q, k, v, e, mode, scale, clip, eps):
+    """The forward as separate PyTorch ops on per-edge tensors, in the order
+    the gattn-triton article's eager reference takes (gather the endpoint
+    rows, the logit, clamp and exp or a max-subtracted exp, scatter-add the
+    weights and the weighted rows, divide): a timing context for the fused
+    kernel, never a result of the library and never used for parity."""
+    N, H, D = q.shape
+    if mode == "clipped":
+        t = (q[dst] * k[src] * scale).clamp(clip[0], clip[1])
+        if e is not None:
+            t = t * e
+        w = t.sum(-1).clamp(clip[0], clip[1]).exp()
+        den = torch.zeros((N, H), dtype=w.dtype, device=q.device).index_add_(0, dst, w) + eps
+    else:
+        t = q[dst] * k[src]
+        if e is not None:
+            t = t * e
+        lg = t.sum(-1) * scale
+        mx = torch.full((N, H), float("-inf"), dtype=lg.dtype, device=q.device)
+        mx = mx.scatter_reduce(0, dst[:, None].expand(-1, H), lg, "amax", include_self=True)
+        w = (lg - mx[dst]).exp()
+        den = torch.zeros((N, H), dtype=w.dtype, device=q.device).index_add_(0, dst, w)
+        den = torch.where(den > 0, den, torch.ones_like(den))
+    num = torch.zeros((N, H, D), dtype=v.dtype, device=q.device).index_add_(0, dst, w[..., None] * v[src])
+    return num / den[..., None]
+
+
+def eager_context(torch, wl, b, fwd_ms_median, reps=20):
+    rp, ci = b.csr.row_ptr, b.csr.col_idx
+    deg = (rp[1:] - rp[:-1]).long()
+    dst = torch.repeat_interleave(torch.arange(wl.num_nodes, device=rp.device), deg)
+    src = ci.long()
+    f = lambda: eager_forward(torch, dst, src, b.q, b.k, b.v, b.e, wl.mode, wl.scale, wl.clip, wl.eps)
+    for _ in range(3):
+        y = f()
+    ts = []
+    for _ in range(reps):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        f()
+        a1.record()
+        torch.cuda.synchronize()
+        ts.append(a0.elapsed_time(a1))
+    ms = float(np.median(ts))
+    diff = float((y.float() - b.out.float()).abs().max())
+    return {"ms_median": round(ms, 5), "speedup_of_fused": round(ms / fwd_ms_median, 2),
+            "max_abs_diff_to_fused": diff, "reps": reps,
+            "formulation": "per-edge gather, logit, exp, index_add_ of weights and weighted rows, divide "
+                           "(PyTorch ops in the input dtype, same device, same CSR)"}
 
 
 # ---------------------------------------------------------------------------
@@ -604,6 +661,9 @@ def main():
            "ms_per_step_with_kernel_events": round(evented_ms / K, 5),
            "build_csr_ms": round(build_ms, 5),
            "gedges_per_s_with_build": round(nnz / ((fwd_ms + build_ms) * 1e-3) / 1e9, 4)}
+    if args.eager and args.variant == "forward":
+        print("# timing the eager PyTorch formulation (context)", file=sys.stderr, flush=True)
+        res["eager_torch"] = eager_context(torch, wl, batches[0], float(np.median(fwd_ms_all)))
     failed = False
     if not args.no_cpu:
         print("# timing the CPU oracle and checking the sampled output rows", file=sys.stderr, flush=True)
