@@ -525,6 +525,7 @@ class Graph:
     col_idx: torch.Tensor      # int32 [nnz]
     edge_perm: torch.Tensor    # int32 [nnz]
     _rw: Optional[RowWindows] = dataclasses.field(default=None, repr=False)
+    _max_degree: Optional[int] = dataclasses.field(default=None, repr=False)
 
     @classmethod
     def from_coo(cls, src: torch.Tensor, dst: torch.Tensor, num_nodes: int, validate: bool = True) -> "Graph":
@@ -542,21 +543,45 @@ class Graph:
             self._rw = gattn_build_rowwindows(self.row_ptr, self.col_idx, self.num_nodes)
         return self._rw
 
+    @property
+    def max_degree(self) -> int:
+        """Largest in-degree (read back once)."""
+        if self._max_degree is None:
+            self._max_degree = int((self.row_ptr[1:] - self.row_ptr[:-1]).max().item()) if self.num_nodes else 0
+        return self._max_degree
+
+    def skewed(self) -> bool:
+        """Whether hubs would set the gather kernel's end under equal
+        destination counts per workgroup: the largest in-degree is above 32x
+        the mean, and the graph is small enough (below 2^24 edges) that its
+        workgroups run in few rounds (in many rounds the other workgroups
+        absorb a hub's)."""
+        if self.num_nodes == 0 or self.nnz == 0 or self.nnz >= (1 << 24):
+            return False
+        return self.max_degree > 32.0 * self.nnz / self.num_nodes
+
 
 def forward(graph: Graph, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, e: Optional[torch.Tensor] = None,
             mode: str = "standard", scale: Optional[float] = None, clip=(-5.0, 5.0), eps: float = 1e-6,
-            path: str = "auto", out: Optional[torch.Tensor] = None, e_out=None, workspace=None):
+            path: str = "auto", out: Optional[torch.Tensor] = None, e_out=None, workspace="auto"):
     """gattn_forward on a Graph.  e (and e_out, when asked for) are indexed
     by the caller's original edge ids -- the COO order from_coo was given --
     and reached through graph.edge_perm, as the gattn-triton article reaches
     its edge tensor through the CSC edge ids.  With fp16 / bf16 inputs, the
     standard mode and no e, paths "auto" and "mfma" use the graph's row
     windows (built on first use); "auto" then takes the MFMA path for dense
-    windows, else the gather path."""
+    windows, else the gather path.  workspace "auto" runs the gather path's
+    balanced partition (heavy rows cut across workgroups) on skewed graphs
+    (Graph.skewed) and the node partition otherwise; None, True or a tensor
+    are passed on to gattn_forward."""
     rw = None
     if path in ("auto", "mfma") and q.dtype != torch.float32 and mode == "standard" and e is None:
         rw = graph.rowwindows()
     ids = graph.edge_perm if (e is not None or (e_out is not None and e_out is not False)) else None
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None, True or a uint8 tensor')
+        workspace = True if graph.skewed() else None
     return gattn_forward(graph.row_ptr, graph.col_idx, q, k, v, e, mode=mode, scale=scale, clip=clip, eps=eps,
                          path=path, rw=rw, out=out, edge_ids=ids, e_out=e_out, workspace=workspace)
 

@@ -87,3 +87,29 @@ def test_from_coo_rejects_bad_indices(gsa):
     dst = torch.tensor([1, 2, 0], dtype=torch.int32, device="cuda")
     with pytest.raises(gsa.GattnError):
         gsa.Graph.from_coo(src, dst, 5)
+
+
+def test_partition_follows_the_degree_skew(gsa):
+    # the power-law graph (in-degrees up to 2000, mean 3.7) takes the balanced
+    # partition, the kNN batch (in-degree 10 everywhere) the node partition;
+    # both bit-identical to the explicit choice
+    c3 = case(3)
+    g3 = gsa.Graph.from_coo(c3.src, c3.dst, c3.wl.num_nodes)
+    assert g3.skewed() and g3.max_degree == int(np.diff(c3.rp).max())
+    out = gsa.forward(g3, c3.q, c3.k, c3.v, scale=c3.wl.scale, path="gather")
+    bal = gsa.gattn_forward(g3.row_ptr, g3.col_idx, c3.q, c3.k, c3.v, scale=c3.wl.scale, path="gather",
+                            workspace=True)
+    assert torch.equal(out, bal)
+    c2 = case(2)
+    g2 = gsa.Graph.from_coo(c2.src, c2.dst, c2.wl.num_nodes)
+    assert not g2.skewed() and g2.max_degree == 10
+    pe = g2.edge_perm.long()
+    e_coo = torch.empty_like(c2.e)
+    e_coo[pe] = c2.e
+    out2 = gsa.forward(g2, c2.q, c2.k, c2.v, e_coo, mode="clipped", scale=c2.wl.scale, clip=c2.wl.clip,
+                       eps=c2.wl.eps)
+    node = gsa.gattn_forward(g2.row_ptr, g2.col_idx, c2.q, c2.k, c2.v, c2.e, mode="clipped", scale=c2.wl.scale,
+                             clip=c2.wl.clip, eps=c2.wl.eps)
+    assert torch.equal(out2, node)
+    with pytest.raises(ValueError):
+        gsa.forward(g2, c2.q, c2.k, c2.v, workspace="balanced")
