@@ -102,10 +102,16 @@ def parse():
 
 
 def src_hash(path_key):
+    """Hash of the kernel sources' code: line comments, trailing blanks and
+    empty lines are left out, so that an edit of a comment does not mark the
+    committed counters as taken on another kernel."""
     h = hashlib.sha256()
     for rel in KERNEL_SRC[path_key]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

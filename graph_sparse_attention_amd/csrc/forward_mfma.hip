@@ -21,8 +21,10 @@
 //   O^T accumulators keep row l%16 in lane l like the softmax state, so the
 //   per-row rescale is a register multiply.
 //
-// S and P never leave the chip.  The work is still bounded by HBM / L2: each
-// K / V row is loaded once per window instead of once per edge.
+// S and P never leave the chip.  What bounds the work is the rate at which
+// the CUs issue the gathers of K and V rows, not the matrix cores: each row
+// is loaded once per window instead of once per edge, and a window's column
+// ids and masks once per window.
 #include "common.hpp"
 #include "internal.hpp"
 
