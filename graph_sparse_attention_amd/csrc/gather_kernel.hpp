@@ -63,7 +63,11 @@
 #define GATTN_GATHER_Q_LDS_BYTES 12288  // Q rows staged per workgroup
 #endif
 #ifndef GATTN_GATHER_Q_LDS_BYTES_SPLIT
-#define GATTN_GATHER_Q_LDS_BYTES_SPLIT 24576  // the same for the balanced partition
+// The same for the balanced partition: 207 rows of 128 B, the most that
+// keeps four workgroups of its 16-bit, 64-wide instantiations on a CU (160 KB
+// of LDS).  A range of many low-degree rows that outgrows the staged rows
+// runs the edge loop that reads Q from global memory, whose waits are coarser.
+#define GATTN_GATHER_Q_LDS_BYTES_SPLIT 26560
 #endif
 #ifndef GATTN_GATHER_EDGES_PER_SLOT
 #define GATTN_GATHER_EDGES_PER_SLOT 3   // target edges per slot, in units of U
