@@ -91,6 +91,18 @@ __device__ __forceinline__ float rows_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)q[0]) + __builtin_bit_cast(float, (uint32_t)q[1]);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest even into one packed register (one
+// v_cvt_pk_{f16,bf16}_f32 on gfx950).
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+}
+
 template <bool BF16>
 __device__ __forceinline__ uint16_t to_bits(float x) {
   if constexpr (BF16) return (uint16_t)bf16_rne(x);
@@ -128,18 +140,39 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
   const int r = lane & 15, g = lane >> 4;
   const int64_t rowstride = (int64_t)a.H * D;
 
-  // B operand of S^T: Q_w^T, lane holds Q[row r][d = 32s + 8g .. +7]
-  u32x4 qf[KS];
-  const int node = 16 * w + r;
+  // The window's Q rows go whole into the wave's second V buffer (rows past
+  // the end read as zeros), 2D bytes per row; the first chunk's wait covers
+  // them, and the B operand of S^T (Q_w^T: lane holds Q[row r][d = 32s + 8g
+  // .. +7]) is read from there before any tile loads into that buffer.
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;  // rows per 64-lane load or store
+  {
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.q, (short)0, (int)a.kv_bytes, kBufferWord3);
 #pragma unroll
-  for (int s = 0; s < KS; ++s)
-    qf[s] = node < a.n ? ld16(a.q + (int64_t)node * rowstride + (int64_t)h * D + 32 * s + 8 * g)
-                       : u32x4{0u, 0u, 0u, 0u};
+    for (int s = 0; s < KS; ++s) {
+      const int row = s * RPI + lane / CPR;
+      const uint32_t off = (uint32_t)((((uint64_t)(16 * w + row) * rowstride + (uint64_t)h * D) * 2)) + 16 * (lane % CPR);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)&s_v[wave][1][s * 1024],
+                                               16, off, 0, 0, 0);
+    }
+  }
+  u32x4 qf[KS];
 
   const int64_t c0 = min<int64_t>(max(a.win_col_ptr[w], 0), a.num_cols) & ~int64_t(15);
   const int64_t c1 = min<int64_t>(max<int64_t>(a.win_col_ptr[w + 1], c0), a.num_cols) & ~int64_t(15);
 
-  float m = -INFINITY, l = 0.f;
+  // Online softmax with a lazily moved reference.  Each row keeps a reference
+  // max m (the same in its four lanes) and each lane a partial sum lp of the
+  // weights of its own columns.  A tile's weights are exp2(x - m); m moves,
+  // and O^T and lp are rescaled, only when a logit exceeds it by more than
+  // 2^kLazy, which after a row's first tile is rare, so most tiles skip the
+  // row-wide max and the rescale (a wave-wide vote decides).  The weights
+  // stay at most 2^kLazy = 256, which fp16 and bf16 hold.  The logit that set
+  // m gives x - m = 0 exactly and weight exp2(0) = 1 exactly (so does the
+  // hardware's exp2), so a row with one edge returns that edge's v bit for bit.
+  constexpr float kLazy = 8.f;
+  float m = -INFINITY, lp = 0.f;
   f32x4 o[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -192,6 +225,7 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
   // sources per row, P^T straight from the accumulator registers, and O^T +=
   // V^T P^T
   auto compute = [&](const u32x4* kf, const uint2* va, uint32_t mask) {
+#pragma clang fp contract(off)  // x - m stays a rounded logit minus m: exactly 0 where x set m
     const uint32_t bits = mask >> (4 * g);
     f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -203,24 +237,25 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
       x[i] = (bits >> i & 1u) ? st[i] * a.scale_l2 : -INFINITY;
       tmax = fmaxf(tmax, x[i]);
     }
-    tmax = rows_max(tmax);
-    const float mn = fmaxf(m, tmax);
-    const float mu = mn == -INFINITY ? 0.f : mn;
-    const float corr = m == mn ? 1.f : fast_exp2(m - mu);  // exp2(0) kept exact
-    float p[4], psum = 0.f;
+    if (__builtin_amdgcn_ballot_w64(tmax > m + kLazy)) {  // wave-uniform
+      const float rmax = rows_max(tmax);
+      const float mn = rmax > m + kLazy ? rmax : m;
+      const float corr = mn == m ? 1.f : fast_exp2(m - mn);  // m = -inf: nothing accumulated yet
+      lp *= corr;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = x[i] == mu ? 1.f : fast_exp2(x[i] - mu);
-      psum += p[i];
+      for (int j = 0; j < NB; ++j) o[j] *= corr;
+      m = mn;
     }
-    psum = rows_sum(psum);
-    l = l * corr + psum;
-    m = mn;
-    uint2 pb;
-    pb.x = (uint32_t)to_bits<BF16>(p[0]) | ((uint32_t)to_bits<BF16>(p[1]) << 16);
-    pb.y = (uint32_t)to_bits<BF16>(p[2]) | ((uint32_t)to_bits<BF16>(p[3]) << 16);
+    const float mu = m == -INFINITY ? 0.f : m;  // a row without an edge so far: every x is -inf
+    float p[4];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) o[j] = mfma_pv<BF16>(va[j], pb, o[j] * corr);
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - mu);
+    lp += (p[0] + p[1]) + (p[2] + p[3]);
+    uint2 pb;
+    pb.x = pack2<BF16>(p[0], p[1]);
+    pb.y = pack2<BF16>(p[2], p[3]);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) o[j] = mfma_pv<BF16>(va[j], pb, o[j]);
   };
   // column c + r's id (lane r's K / V source) and the mask of row r of tile
   // c / 16, c counted from the start of the staged chunk
@@ -248,6 +283,11 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (cb == c0) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        qf[s] = *reinterpret_cast<const u32x4*>(&s_v[wave][1][r * 2 * D + 64 * s + 16 * g]);
+    }
     int32_t colA, colB = -1;
     uint32_t maskA = 0, maskB = 0;
     u32x4 kA[KS], kB[KS];
@@ -278,17 +318,30 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
     }
   }
 
-  // O[row][d = 16j + 4g + i] = O^T[d][row] / l  (row without edges -> 0)
-  if (node < a.n) {
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-    uint16_t* dst = a.out + (int64_t)node * rowstride + (int64_t)h * D + 4 * g;
+  // O[row][d = 16j + 4g + i] = O^T[d][row] / l  (row without edges -> 0).
+  // The rows go through the wave's V buffers (every load into them has been
+  // waited for) so that each store instruction writes whole 2D-byte rows.
+  const float l = rows_sum(lp);
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // a window without columns still has its Q rows in flight
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  constexpr int RS = 2 * D + 16;  // padded row stride in LDS (bytes)
+  static_assert(16 * RS <= 2 * VB, "the output rows fit the wave's V buffers");
+  uint8_t* so = &s_v[wave][0][0];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      uint2 w2;
-      w2.x = (uint32_t)to_bits<BF16>(o[j][0] * inv) | ((uint32_t)to_bits<BF16>(o[j][1] * inv) << 16);
-      w2.y = (uint32_t)to_bits<BF16>(o[j][2] * inv) | ((uint32_t)to_bits<BF16>(o[j][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(dst + 16 * j) = w2;
-    }
+  for (int j = 0; j < NB; ++j) {
+    uint2 w2;
+    w2.x = pack2<BF16>(o[j][0] * inv, o[j][1] * inv);
+    w2.y = pack2<BF16>(o[j][2] * inv, o[j][3] * inv);
+    *reinterpret_cast<uint2*>(so + r * RS + 2 * (16 * j + 4 * g)) = w2;
+  }
+#pragma unroll
+  for (int q = 0; q < 16 / RPI; ++q) {
+    const int row = q * RPI + lane / CPR, ch = lane % CPR;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(so + row * RS + 16 * ch);
+    const int nd = 16 * w + row;
+    if (nd < a.n) st16(a.out + (int64_t)nd * rowstride + (int64_t)h * D + 8 * ch, x);
   }
 }
 
