@@ -21,10 +21,10 @@
 //   O^T accumulators keep row l%16 in lane l like the softmax state, so the
 //   per-row rescale is a register multiply.
 //
-// S and P never leave the chip.  What bounds the work is the rate at which
-// the CUs issue the gathers of K and V rows, not the matrix cores: each row
-// is loaded once per window instead of once per edge, and a window's column
-// ids and masks once per window.
+// S and P never leave the chip.  What bounds the work is the memory traffic
+// and its latency, not the matrix cores: each K / V row is loaded once per
+// window instead of once per edge, a window's column ids and masks once per
+// window, and every load and store moves whole rows.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -113,21 +113,27 @@ __device__ __forceinline__ uint16_t to_bits(float x) {
 // keeps at or below 2^31 bytes, so no offset wraps around.
 constexpr uint32_t kPastEnd = 0x80000000u;
 
-// Two tiles in flight per wave: while tile t computes, tile t + 1's K rows
-// (registers) and V rows (LDS) are loading.  V goes straight from memory into
-// one of two per-wave LDS buffers (direct-to-LDS loads, no registers), and
-// tile t reads its V^T from its buffer into registers before tile t + 1's
-// loads are issued, so the wait that precedes that read covers only loads
-// the tile needs anyway.  K and V are addressed through buffer resources: a
-// padding column's loads fall past the end, return zeros and reach no memory.
+// Every global access moves whole rows: a tile's K and V rows, the window's
+// Q rows and its output rows each go through per-wave LDS buffers, so one
+// 64-lane instruction covers 512 / D whole rows instead of a 32- or 64-byte
+// piece of each of sixteen rows (the operand layouts of the matrix cores);
+// this alone took config-5-sized batches from 41.7 to 33.3 us.  Two tiles in
+// flight per wave: while tile t computes, tile t + 1's rows are loading into
+// the other pair of buffers (direct-to-LDS loads, no registers); tile t reads
+// its operands from LDS before tile t + 1's loads are issued, so the wait
+// that precedes those reads covers only loads the tile needs anyway.  K, V
+// and Q are addressed through buffer resources: a padding column's (or a
+// row past the end's) loads fall past the end, return zeros and reach no
+// memory.
 template <bool BF16, int D>
 // The second launch bound (at least 2 waves per SIMD) makes the compiler pack
 // the registers.
 __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
   constexpr int KS = D / 32;   // 16x16x32 steps for S^T
   constexpr int NB = D / 16;   // 16-wide d blocks for O^T
-  constexpr int VB = KS * 1024;  // one tile's V rows in LDS: KS loads of 64 lanes x 16 bytes
+  constexpr int VB = KS * 1024;  // one tile's K (or V) rows in LDS: KS loads of 64 lanes x 16 bytes
   __shared__ __attribute__((aligned(16))) uint8_t s_v[kWavesPerWg][2][VB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[kWavesPerWg][2][VB];
   // a wave's window: column ids and masks of up to kMetaCols / 16 tiles at a time
   __shared__ int32_t s_col[kWavesPerWg][kMetaCols];
   __shared__ uint32_t s_msk[kWavesPerWg][kMetaCols / 2];  // two 16-bit masks per word
@@ -179,46 +185,51 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
 
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)a.k, (short)0, (int)a.kv_bytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)a.v, (short)0, (int)a.kv_bytes, kBufferWord3);
-  // lane (r, g)'s byte offset of column col's row, head h, d = 8g (per step s: + 64 s)
-  auto row_off = [&](int32_t col) -> uint32_t {
-    return (uint32_t)col < (uint32_t)a.n ? (uint32_t)(((uint64_t)col * rowstride + (uint64_t)h * D + 8 * g) * 2)
-                                         : kPastEnd;
-  };
-  // tile loads: K rows into registers, V rows into LDS buffer vb, where lane
-  // (r, g) of step s writes V[column r][d = 32s + 8g .. +7] at byte 16 (16 g + r)
-  // of the step's 1024-byte block
-  auto issue = [&](int32_t col, u32x4* kk, int vb) {
-    const uint32_t off = row_off(col);
+  // A tile's K and V rows land in LDS row-major, 2D bytes per row, each
+  // 64-lane load covering RPI whole rows (lane l: row l / CPR of the load,
+  // 16-byte chunk slot l % CPR).  Slot p of row t holds chunk p ^ (t % CPR),
+  // which spreads the column reads below over the LDS banks.
+  auto slot = [&](int row, int chunk) { return row * 2 * D + 16 * (chunk ^ (row % CPR)); };
+  auto issue = [&](int32_t c, int b) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      kk[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off + 64 * s, 0, 0));
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)&s_v[wave][vb][s * 1024],
-                                               16, off + 64 * s, 0, 0, 0);
+    for (int s = 0; s < KS; ++s) {
+      const int row = s * RPI + lane / CPR;
+      const int32_t col = s_col[wave][c + row];
+      const uint32_t off = (uint32_t)col < (uint32_t)a.n
+                               ? (uint32_t)(((uint64_t)col * rowstride + (uint64_t)h * D) * 2) +
+                                     16 * ((lane % CPR) ^ (row % CPR))
+                               : kPastEnd;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)&s_k[wave][b][s * 1024],
+                                               16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)&s_v[wave][b][s * 1024],
+                                               16, off, 0, 0, 0);
+    }
   };
-  // V^T operand of d block j: lane (i = lane % 16, q = lane / 16) takes
-  // V[source 4q + t][d = 16j + i], t = 0..3, from one transposing LDS read.
-  // That read hands lane i of each 16-lane group element i % 4 of the 8 bytes
-  // addressed by lane 4t + i / 4 of the group; so lane k of group q addresses
-  // V[source 4q + k / 4][d = 16j + 4 (k % 4) .. +3], 8 contiguous bytes of
-  // the 16 that one direct-to-LDS lane wrote.
-  auto read_vt = [&](int vb, uint2* va) {
+  // Operands of tile buffer b.  K (A operand of S^T): lane (r, g) takes
+  // K[source r][d = 32s + 8g .. +7], chunk 4s + g of row r.  V^T (A operand of
+  // O^T, d block j): lane (i = lane % 16, q = lane / 16) takes V[source 4q +
+  // t][d = 16j + i], t = 0..3, from one transposing LDS read, which hands
+  // lane i of each 16-lane group element i % 4 of the 8 bytes addressed by
+  // lane 4t + i / 4 of the group; so lane k of group q addresses V[source 4q
+  // + k / 4][d = 16j + 4 (k % 4) .. +3], half of one 16-byte chunk.
+  auto read_tile = [&](int b, u32x4* kf, uint2* va) {
     // The compiler does not order these LDS reads after the direct-to-LDS
-    // loads that fill the buffer: wait for every load in flight explicitly
-    // (here they are all this tile's rows or the next tile's column ids),
-    // with compiler fences so that no read moves above the wait.
+    // loads that fill the buffers: wait for every load in flight explicitly
+    // (here they are all this tile's rows), with compiler fences so that no
+    // read moves above the wait.
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kf[s] = *reinterpret_cast<const u32x4*>(&s_k[wave][b][slot(r, 4 * s + g)]);
     const int src = 4 * g + (r >> 2);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int d0 = 16 * j + 4 * (r & 3);
-      const int byte = (d0 >> 5) * 1024 + 16 * (16 * ((d0 & 31) >> 3) + src) + 2 * (d0 & 7);
+      const int byte = slot(src, d0 >> 3) + 2 * (d0 & 7);
       va[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                             (__attribute__((address_space(3))) i16x4*)(
-                                                (__attribute__((address_space(3))) uint8_t*)&s_v[wave][vb][0] + byte)));
+                                                (__attribute__((address_space(3))) uint8_t*)&s_v[wave][b][0] + byte)));
     }
   };
   // one tile: S^T on the matrix cores, the online softmax over the tile's 16
@@ -257,12 +268,8 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) o[j] = mfma_pv<BF16>(va[j], pb, o[j]);
   };
-  // column c + r's id (lane r's K / V source) and the mask of row r of tile
-  // c / 16, c counted from the start of the staged chunk
-  auto meta = [&](int32_t c, int32_t& col, uint32_t& mask) {
-    col = s_col[wave][c + r];
-    mask = reinterpret_cast<const uint16_t*>(s_msk[wave])[c + r];
-  };
+  // the mask of row r of tile c / 16, c counted from the start of the staged chunk
+  auto mask_of = [&](int32_t c) -> uint32_t { return reinterpret_cast<const uint16_t*>(s_msk[wave])[c + r]; };
 
   // The window's ids and masks go to LDS once per chunk of up to 16 tiles, 64
   // ids or 128 masks per direct-to-LDS load (lane l's 4 bytes land at 4 l),
@@ -288,33 +295,26 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
       for (int s = 0; s < KS; ++s)
         qf[s] = *reinterpret_cast<const u32x4*>(&s_v[wave][1][r * 2 * D + 64 * s + 16 * g]);
     }
-    int32_t colA, colB = -1;
-    uint32_t maskA = 0, maskB = 0;
-    u32x4 kA[KS], kB[KS];
+    uint32_t maskA = mask_of(0), maskB = 0;
+    u32x4 kf[KS];
     uint2 va[NB];
-    meta(0, colA, maskA);
-    if (16 < n) meta(16, colB, maskB);
-    issue(colA, kA, 0);
-    // tiles c (set A, buffer 0) and c + 16 (set B, buffer 1) of the chunk per pass; the
-    // branches are uniform across the wave
+    issue(0, 0);
+    // tiles c (buffers 0) and c + 16 (buffers 1) per pass: a tile's rows load
+    // while the one before it computes.  The branches are uniform across the wave.
     for (int32_t c = 0; c < n; c += 32) {
-      read_vt(0, va);
-      if (c + 16 < n) issue(colB, kB, 1);
-      int32_t colA2 = -1;
-      uint32_t maskA2 = 0;
-      if (c + 32 < n) meta(c + 32, colA2, maskA2);
-      compute(kA, va, maskA);
+      read_tile(0, kf, va);
+      if (c + 16 < n) {
+        maskB = mask_of(c + 16);
+        issue(c + 16, 1);
+      }
+      compute(kf, va, maskA);
       if (c + 16 >= n) break;
-      read_vt(1, va);
-      if (c + 32 < n) issue(colA2, kA, 0);
-      int32_t colB2 = -1;
-      uint32_t maskB2 = 0;
-      if (c + 48 < n) meta(c + 48, colB2, maskB2);
-      compute(kB, va, maskB);
-      colA = colA2;
-      colB = colB2;
-      maskA = maskA2;
-      maskB = maskB2;
+      read_tile(1, kf, va);
+      if (c + 32 < n) {
+        maskA = mask_of(c + 32);
+        issue(c + 32, 0);
+      }
+      compute(kf, va, maskB);
     }
   }
 
