@@ -34,6 +34,7 @@ namespace {
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWavesPerWg = 4;
 constexpr int kMetaCols = 256;  // column ids (and masks) a wave stages in LDS at a time
@@ -117,14 +118,14 @@ constexpr uint32_t kPastEnd = 0x80000000u;
 // Q rows and its output rows each go through per-wave LDS buffers, so one
 // 64-lane instruction covers 512 / D whole rows instead of a 32- or 64-byte
 // piece of each of sixteen rows (the operand layouts of the matrix cores);
-// this alone took config-5-sized batches from 41.7 to 33.3 us.  Two tiles in
-// flight per wave: while tile t computes, tile t + 1's rows are loading into
-// the other pair of buffers (direct-to-LDS loads, no registers); tile t reads
-// its operands from LDS before tile t + 1's loads are issued, so the wait
-// that precedes those reads covers only loads the tile needs anyway.  K, V
-// and Q are addressed through buffer resources: a padding column's (or a
-// row past the end's) loads fall past the end, return zeros and reach no
-// memory.
+// on 1024 complete digraphs of 20-40 nodes (8 heads, D = 64) this alone
+// took the kernel from 41.7 to 33.3 us.  Two tiles in flight per wave: tile
+// t + 1's rows are issued into the other pair of buffers (direct-to-LDS
+// loads, no registers) before the wave waits for tile t's, so they load
+// while tile t computes; the wait counts exactly the loads issued after
+// tile t's.  K, V and Q are addressed through buffer resources: a padding
+// column's (or a row past the end's) loads fall past the end, return zeros
+// and reach no memory.
 template <bool BF16, int D>
 // The second launch bound (at least 2 waves per SIMD) makes the compiler pack
 // the registers.
@@ -189,6 +190,27 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
   // 64-lane load covering RPI whole rows (lane l: row l / CPR of the load,
   // 16-byte chunk slot l % CPR).  Slot p of row t holds chunk p ^ (t % CPR),
   // which spreads the column reads below over the LDS banks.
+  // K and V descriptors as raw words (base, num_records, flags) for the
+  // direct-to-LDS loads below
+  const uint64_t kbase = (uint64_t)a.k, vbase = (uint64_t)a.v;
+  const i32x4 dk = {(int)(uint32_t)kbase, (int)(uint32_t)(kbase >> 32) & 0xffff, (int)a.kv_bytes, kBufferWord3};
+  const i32x4 dv = {(int)(uint32_t)vbase, (int)(uint32_t)(vbase >> 32) & 0xffff, (int)a.kv_bytes, kBufferWord3};
+  // One 16-byte direct-to-LDS load per lane: lane l's bytes land at LDS
+  // address lds + 16 l.  Written as asm because the compiler, which cannot
+  // tell the two buffer pairs apart, would otherwise make every LDS read
+  // wait for all such loads in flight (the next tile's included); every wait
+  // for these loads is explicit instead (wait_vm).
+  auto dma16 = [&](const i32x4& d, uint32_t voff, const void* lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is set here, not preserved
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(d)
+                 : "memory", "m0");
+#pragma clang diagnostic pop
+  };
   auto slot = [&](int row, int chunk) { return row * 2 * D + 16 * (chunk ^ (row % CPR)); };
   auto issue = [&](int32_t c, int b) {
 #pragma unroll
@@ -199,10 +221,8 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
                                ? (uint32_t)(((uint64_t)col * rowstride + (uint64_t)h * D) * 2) +
                                      16 * ((lane % CPR) ^ (row % CPR))
                                : kPastEnd;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)&s_k[wave][b][s * 1024],
-                                               16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)&s_v[wave][b][s * 1024],
-                                               16, off, 0, 0, 0);
+      dma16(dk, off, &s_k[wave][b][s * 1024]);
+      dma16(dv, off, &s_v[wave][b][s * 1024]);
     }
   };
   // Operands of tile buffer b.  K (A operand of S^T): lane (r, g) takes
@@ -213,13 +233,6 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
   // lane 4t + i / 4 of the group; so lane k of group q addresses V[source 4q
   // + k / 4][d = 16j + 4 (k % 4) .. +3], half of one 16-byte chunk.
   auto read_tile = [&](int b, u32x4* kf, uint2* va) {
-    // The compiler does not order these LDS reads after the direct-to-LDS
-    // loads that fill the buffers: wait for every load in flight explicitly
-    // (here they are all this tile's rows), with compiler fences so that no
-    // read moves above the wait.
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
     for (int s = 0; s < KS; ++s) kf[s] = *reinterpret_cast<const u32x4*>(&s_k[wave][b][slot(r, 4 * s + g)]);
     const int src = 4 * g + (r >> 2);
@@ -268,6 +281,16 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) o[j] = mfma_pv<BF16>(va[j], pb, o[j]);
   };
+  // wait until at most N direct-to-LDS loads of this wave are in flight (they
+  // complete in order), with compiler fences so that no LDS access crosses it
+  auto wait_vm = [&](auto n_) {
+    constexpr int N = decltype(n_)::value;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+  using kTile = std::integral_constant<int, 2 * KS>;
+  using kNone = std::integral_constant<int, 0>;
   // the mask of row r of tile c / 16, c counted from the start of the staged chunk
   auto mask_of = [&](int32_t c) -> uint32_t { return reinterpret_cast<const uint16_t*>(s_msk[wave])[c + r]; };
 
@@ -302,18 +325,24 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
     // tiles c (buffers 0) and c + 16 (buffers 1) per pass: a tile's rows load
     // while the one before it computes.  The branches are uniform across the wave.
     for (int32_t c = 0; c < n; c += 32) {
-      read_tile(0, kf, va);
       if (c + 16 < n) {
         maskB = mask_of(c + 16);
         issue(c + 16, 1);
+        wait_vm(kTile{});
+      } else {
+        wait_vm(kNone{});
       }
+      read_tile(0, kf, va);
       compute(kf, va, maskA);
       if (c + 16 >= n) break;
-      read_tile(1, kf, va);
       if (c + 32 < n) {
         maskA = mask_of(c + 32);
         issue(c + 32, 0);
+        wait_vm(kTile{});
+      } else {
+        wait_vm(kNone{});
       }
+      read_tile(1, kf, va);
       compute(kf, va, maskB);
     }
   }
