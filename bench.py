@@ -80,7 +80,7 @@ def parse():
     p.add_argument("--config", type=int, default=4,
                    help="1-5: the benchmark configurations; 6: the mixed-density batch of the hybrid dispatch")
     p.add_argument("--path", default="auto", choices=["auto", "gather", "mfma", "hybrid"])
-    p.add_argument("--min-density", type=float, default=0.125, help="hybrid path: tile density of an MFMA window")
+    p.add_argument("--min-density", type=float, default=0.09, help="hybrid path: tile density of an MFMA window")
     p.add_argument("--variant", default="forward", choices=list(VARIANTS))
     p.add_argument("--partition", default="node", choices=["balanced", "node"],
                    help="gather path: edge-balanced workgroups with cut heavy rows (workspace) or equal node counts")

@@ -280,7 +280,7 @@ class Hybrid:
 
 
 def gattn_build_hybrid(row_ptr: torch.Tensor, col_idx: torch.Tensor, rw: RowWindows, q: torch.Tensor,
-                       min_density: float = 0.125) -> Hybrid:
+                       min_density: float = 0.09) -> Hybrid:
     """Row windows whose tile density (edges / (16 * columns)) is at least
     min_density go to the MFMA path, the other rows to the gather path, in
     ranges sized like its workgroups.  q gives the geometry (N, H, D, dtype);

@@ -118,11 +118,15 @@ def test_forward_argument_errors(gsa):
 
 def test_path_resolution(gsa):
     base = 1 << 32
-    rw = gsa._RowWindows(7, 16 * 20, base + (10 << 20), base + (11 << 20), base + (12 << 20))  # density 1000/(16*320)
+    rw = gsa._RowWindows(7, 16 * 80, base + (10 << 20), base + (11 << 20), base + (12 << 20))  # density 1000/(16*1280)
     a = fake_args(gsa)
     assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_GATHER)           # no row windows
     a.rw = ctypes.pointer(rw)
-    assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_GATHER)           # density 0.195 < 0.25
+    assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_GATHER)           # density 0.049 < 0.09
+    rw.num_cols = 16 * 60                                                     # density 0.065 < 0.09
+    assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_GATHER)
+    rw.num_cols = 16 * 40                                                     # density 0.098
+    assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_MFMA)
     rw.num_cols = 16 * 10                                                     # density 0.39
     assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_MFMA)
     a.e = base + (14 << 20)

@@ -110,6 +110,22 @@ def test_hybrid_mixed_workload(gsa):
     print(f"mixed workload hybrid: {hy.num_dense} dense windows, {hy.num_ranges} ranges, rel-L2 {err:.3e}")
 
 
+def test_auto_path_density_rule(gsa):
+    # Without a plan, AUTO takes the MFMA path for row windows whose tiles are
+    # at least 9% full overall: the mixed batch (about 12%) goes to the matrix
+    # cores, the power-law graph (about 6%, with hubs) stays gathered
+    for cfg, want in ((6, "mfma"), (3, "gather")):
+        wl = W.make(cfg)
+        rp, ci, _ = oracle.build_csr(wl.num_nodes, wl.src, wl.dst)
+        rp_t, ci_t = torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda()
+        q = W.cast(wl.q(), wl.dtype).cuda()
+        rw = gsa.gattn_build_rowwindows(rp_t, ci_t, wl.num_nodes)
+        density = wl.nnz / (16.0 * rw.num_cols)
+        print(f"config {cfg}: tile density {density:.3f}", flush=True)
+        assert (density >= 0.09) == (want == "mfma")
+        assert gsa.gattn_forward_path(rp_t, ci_t, q, q, q, rw=rw) == want
+
+
 def test_hybrid_errors(gsa):
     n, rp, ci, q, k, v = mixed_inputs(4, 2, 32, "f16", 9)
     rp_t, ci_t = torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda()
