@@ -112,6 +112,33 @@ def test_matrix_mfma(gsa, dtype, hd, n):
     check_forward(out, ref, mag, dtype)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", ["wide", "rising"])
+def test_mfma_logit_ranges(gsa, dtype, shape):
+    # The MFMA kernel moves a row's reference max only when a logit exceeds it
+    # by more than 2^8 (log2 units), rescaling the row's sums then.  "wide":
+    # logits with a spread of tens of natural units, so references move on
+    # most tiles; "rising": every later column (sorted, so every later tile)
+    # has a larger logit, so every tile of a long row moves the reference.
+    n, h, d = 300, 2, 64
+    rp, ci, q, k, v, _ = small_case(n, 48 if shape == "wide" else 150, h, d, dtype, "standard", False, 71)
+    if shape == "wide":
+        q, k = W.cast(q.float().numpy() * 4, dtype), W.cast(k.float().numpy() * 4, dtype)
+    else:
+        u = np.random.default_rng(5).standard_normal((h, d)).astype(np.float32)
+        u /= np.linalg.norm(u, axis=1, keepdims=True)
+        q = W.cast(np.broadcast_to(u * 8.0, (n, h, d)).copy(), dtype)
+        ramp = np.linspace(0.0, 60.0, n, dtype=np.float32)[:, None, None]
+        k = W.cast(ramp * u[None], dtype)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    ref, mag = oracle.forward(rp, ci, oracle.widen(q), oracle.widen(k), oracle.widen(v), scale=scale, want_mag=True)
+    rp_t, ci_t = torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda()
+    rw = gsa.gattn_build_rowwindows(rp_t, ci_t, n)
+    out = gsa.gattn_forward(rp_t, ci_t, q.cuda(), k.cuda(), v.cuda(), scale=scale, path="mfma", rw=rw)
+    assert torch.isfinite(out).all()
+    check_forward(out, ref, mag, dtype)
+
+
 @pytest.mark.parametrize("path", ["gather", "gather-node", "mfma"])
 def test_hubs_and_isolated(gsa, path):
     # destinations far above a workgroup's share (split over all slots and
