@@ -22,9 +22,11 @@ static_assert(kStaticScratchBytes == GATTN_NOALLOC_SCRATCH_BYTES, "scratch size 
 namespace {
 
 // AUTO: nnz / (256 * tiles) at or above -> MFMA.  Measured crossover of the
-// two kernels: uniformly random sparse rows (tiles 1/16 full) run faster
-// gathered, a batch whose tiles are 12% full (half complete digraphs, half
-// sparse blocks) 1.6x faster on the matrix cores.
+// two kernels: uniformly random sparse rows (tiles 1/16 full) run no faster
+// on the matrix cores and a power-law graph with hub rows (whose windows
+// hold up to 2000 columns for one wave) slower, while a batch whose tiles
+// are 12% full (half complete digraphs, half sparse blocks) runs 1.6x faster
+// there.
 constexpr double kMfmaMinDensity = 0.09;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }

@@ -50,6 +50,7 @@ struct MfmaArgs {
   const int32_t* __restrict__ windows;  // nullable: the grid's windows (a hybrid plan's dense ones)
   int64_t num_cols;
   int32_t n, H, W;
+  int32_t nwb;        // windows in the grid (W, or the hybrid plan's dense ones)
   float scale_l2;     // scale * log2(e)
   uint32_t kv_bytes;  // bytes of K (and of V), at most 2^31
 };
@@ -140,10 +141,22 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
   __shared__ uint32_t s_msk[kWavesPerWg][kMetaCols / 2];  // two 16-bit masks per word
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wb = (int)xcd_contiguous_block(blockIdx.x, gridDim.x);
+  // A workgroup's waves: heads h0 .. h0 + 3 of one window when there are at
+  // least 4 heads (grid y = head group); with fewer, consecutive (window,
+  // head) items, heads fastest, so that no wave of a workgroup sits idle.
+  const int lin = (int)xcd_contiguous_block(blockIdx.x, gridDim.x);
+  int wb, h;
+  if (a.H >= kWavesPerWg) {
+    wb = lin;
+    h = blockIdx.y * kWavesPerWg + wave;
+  } else {
+    const int item = __builtin_amdgcn_readfirstlane(lin * kWavesPerWg + wave);  // wave-uniform
+    wb = item / a.H;
+    h = item - wb * a.H;
+  }
+  if (h >= a.H || wb >= a.nwb) return;
   const int w = a.windows ? a.windows[wb] : wb;
-  const int h = blockIdx.y * kWavesPerWg + wave;
-  if (h >= a.H || w < 0 || w >= a.W) return;
+  if (w < 0 || w >= a.W) return;
   const int r = lane & 15, g = lane >> 4;
   const int64_t rowstride = (int64_t)a.H * D;
 
@@ -376,7 +389,9 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
 
 template <bool BF16>
 hipError_t launch_b(const gattn_forward_args& fa, const MfmaArgs& ma, int32_t blocks, hipStream_t s) {
-  dim3 grid((unsigned)blocks, (unsigned)ceil_div(fa.num_heads, kWavesPerWg));
+  const dim3 grid = fa.num_heads >= kWavesPerWg
+                       ? dim3((unsigned)blocks, (unsigned)ceil_div(fa.num_heads, kWavesPerWg))
+                       : dim3((unsigned)ceil_div((int64_t)blocks * fa.num_heads, kWavesPerWg));
   dim3 block(kWavesPerWg * 64);
   switch (fa.head_dim) {
     case 32: hipLaunchKernelGGL((mfma_kernel<BF16, 32>), grid, block, 0, s, ma); break;
@@ -413,6 +428,7 @@ hipError_t launch_forward_mfma(const gattn_forward_args& fa, const int32_t* wind
   ma.scale_l2 = fa.scale * kLog2e;
   ma.kv_bytes = (uint32_t)((uint64_t)fa.num_nodes * fa.num_heads * fa.head_dim * 2);
   const int32_t blocks = windows ? num_windows : ma.W;
+  ma.nwb = blocks;
   return fa.dtype == GATTN_BF16 ? launch_b<true>(fa, ma, blocks, s) : launch_b<false>(fa, ma, blocks, s);
 }
 
