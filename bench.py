@@ -93,6 +93,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle (and with it the parity check)")
     p.add_argument("--eager", action="store_true",
                    help="also time an eager PyTorch formulation of the same forward (context only)")
+    p.add_argument("--ceiling", action="store_true",
+                   help="gather rate against the size of the gathered table (graphs shaped like config 4)")
     p.add_argument("--counters-run", action="store_true")
     p.add_argument("--ingest-counters", default=None)
     args = p.parse_args()
@@ -445,12 +447,61 @@ def ingest_counters(dirname, config, path_key, variant="forward", partition="nod
 
 # ---------------------------------------------------------------------------
 
+def ceiling():
+    """The gather kernel on graphs shaped like config 4 (2.45M destinations of
+    in-degree 41, H = 1, D = 64, bf16, standard softmax) whose sources are
+    drawn uniformly from the first S nodes, S chosen so that the K and V rows
+    that can be gathered take 16 MB ... 627 MB (all nodes): the rate of the
+    gathered rows (B_gather per launch over the mean launch time) against the
+    size of the table they come from.  If the caches on the chip served random
+    128-byte rows faster than HBM, the smaller tables would run faster."""
+    import torch
+    import graph_sparse_attention_amd as gsa
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    N, deg, D = 2_450_000, 41, 64
+    nnz = N * deg
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    q, k, v = (torch.randn(N, 1, D, device=dev, generator=g).to(torch.bfloat16) for _ in range(3))
+    out = torch.empty_like(q)
+    dst = torch.arange(N, device=dev, dtype=torch.int32).repeat_interleave(deg)
+    rows = []
+    for table_mb in (16, 32, 64, 128, 256, 627):
+        S = min(N, (table_mb << 20) // (2 * D * 2 * 1))  # K and V: 2 D bytes each per node
+        src = torch.randint(0, S, (nnz,), device=dev, dtype=torch.int32, generator=g)
+        rp, ci, _ = gsa.gattn_build_csr(src, dst, N)
+        del src
+        f = lambda: gsa.gattn_forward(rp, ci, q, k, v, scale=1 / math.sqrt(D), path="gather", out=out)
+        for _ in range(3):
+            f()
+        ts = []
+        for _ in range(10):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        t = sum(ts) / len(ts)
+        b_gather = nnz * 2 * D * 2
+        rows.append({"table_mb": round(S * 4 * D / 2**20, 1), "sources": S, "ms": round(t * 1e3, 4),
+                     "gathered_tb_s": round(b_gather / t / 1e12, 3), "frac_gather": round(b_gather / t / 8e12, 4)})
+        print(f"# K/V table {rows[-1]['table_mb']} MB ({S} sources): {t * 1e3:.3f} ms, "
+              f"{b_gather / t / 1e12:.2f} TB/s of gathered rows", file=sys.stderr, flush=True)
+        del rp, ci
+    print(json.dumps({"ceiling": rows, "edges": nnz, "destinations": N}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the library has no multi-GPU path; "
               "each GPU would build and run the graphs of its own share of the batch.", file=sys.stderr)
         sys.exit(2)
+    if args.ceiling:
+        ceiling()
+        return
     import workloads as W
     if args.ingest_counters:
         path_key = args.path if args.path in ("mfma", "hybrid") else "gather"
