@@ -105,12 +105,6 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   else return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
 }
 
-template <bool BF16>
-__device__ __forceinline__ uint16_t to_bits(float x) {
-  if constexpr (BF16) return (uint16_t)bf16_rne(x);
-  else return __builtin_bit_cast(uint16_t, (_Float16)x);
-}
-
 // Offset of a padding column's loads: past the end of K and V, which the host
 // keeps at or below 2^31 bytes, so no offset wraps around.
 constexpr uint32_t kPastEnd = 0x80000000u;
@@ -197,8 +191,6 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
 #pragma unroll
   for (int j = 0; j < NB; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)a.k, (short)0, (int)a.kv_bytes, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)a.v, (short)0, (int)a.kv_bytes, kBufferWord3);
   // A tile's K and V rows land in LDS row-major, 2D bytes per row, each
   // 64-lane load covering RPI whole rows (lane l: row l / CPR of the load,
   // 16-byte chunk slot l % CPR).  Slot p of row t holds chunk p ^ (t % CPR),
