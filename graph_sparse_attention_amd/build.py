@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "scan.hip", "build_csr.hip", "build_csr_radix.hip", "build_rowwindows.hip", "forward_gather.hip",
-           "forward_gather_split.hip", "forward_mfma.hip", "noalloc.hip"]
+           "forward_gather_split.hip", "forward_mfma.hip", "noalloc.hip", "validate.hip"]
 
 COMMON = ["-O3", "-fPIC", "-fvisibility=hidden", "-std=c++17", "-Wall", "-Wno-unused-function", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC]

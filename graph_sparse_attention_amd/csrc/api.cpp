@@ -188,26 +188,21 @@ gattn_status resolve(const gattn_forward_args* a, gattn_path* out) {
   return GATTN_OK;
 }
 
-// GATTN_FLAG_VALIDATE: copy the index arrays to the host and check them.
-// ids (nullable) must lie in [0, nnz); with `permutation` each id once.
+// GATTN_FLAG_VALIDATE: row pointers, column indices and the edge-id map
+// (nullable; values in [0, nnz)) checked on the device; with `permutation`
+// each id must also occur once, which is checked on the host (a copy of the
+// ids; only the edge update, whose rows two positions must not share, asks).
 gattn_status validate_graph(int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
                             const int32_t* ids, bool permutation, hipStream_t s) {
-  std::vector<int32_t> rp((size_t)n + 1), ci((size_t)nnz), id(ids ? (size_t)nnz : 0);
-  if (hipMemcpyAsync(rp.data(), row_ptr, rp.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess) return GATTN_ERR_HIP;
-  if (nnz && hipMemcpyAsync(ci.data(), col_idx, ci.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess)
-    return GATTN_ERR_HIP;
-  if (nnz && ids && hipMemcpyAsync(id.data(), ids, id.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess)
-    return GATTN_ERR_HIP;
-  if (hipStreamSynchronize(s) != hipSuccess) return GATTN_ERR_HIP;
-  if (rp[0] != 0 || rp[n] != nnz) return GATTN_ERR_BAD_GRAPH;
-  for (int32_t i = 0; i < n; ++i)
-    if (rp[i + 1] < rp[i]) return GATTN_ERR_BAD_GRAPH;
-  for (int32_t c : ci)
-    if (c < 0 || c >= n) return GATTN_ERR_BAD_GRAPH;
-  std::vector<uint8_t> seen(permutation ? id.size() : 0, 0);
-  for (int32_t r : id) {
-    if (r < 0 || r >= nnz) return GATTN_ERR_BAD_GRAPH;
-    if (permutation) {
+  bool ok = false;
+  if (validate_on_device(n, nnz, row_ptr, col_idx, ids, s, &ok) != hipSuccess) return GATTN_ERR_HIP;
+  if (!ok) return GATTN_ERR_BAD_GRAPH;
+  if (permutation && ids && nnz > 0) {
+    std::vector<int32_t> id((size_t)nnz);
+    if (hipMemcpyAsync(id.data(), ids, id.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess) return GATTN_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return GATTN_ERR_HIP;
+    std::vector<uint8_t> seen(id.size(), 0);
+    for (int32_t r : id) {  // in range: checked above
       if (seen[r]) return GATTN_ERR_BAD_GRAPH;
       seen[r] = 1;
     }

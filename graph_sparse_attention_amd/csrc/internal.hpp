@@ -49,6 +49,10 @@ hipError_t launch_rowwindows_fill(int32_t n, int64_t nnz, const int32_t* row_ptr
 
 // Forward -------------------------------------------------------------------
 hipError_t launch_forward_gather(const gattn_forward_args& a, hipStream_t s);
+// GATTN_FLAG_VALIDATE's range checks of row_ptr, col_idx and the edge-id map
+// (nullable) on the device; synchronizes the stream, *ok tells the result.
+hipError_t validate_on_device(int32_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                              const int32_t* ids, hipStream_t s, bool* ok);
 // windows: nullable list of the windows to run (count num_windows); else all
 hipError_t launch_forward_mfma(const gattn_forward_args& a, const int32_t* windows, int32_t num_windows, hipStream_t s);
 // gather over given (first row, row count) ranges of at most range_rows rows

@@ -92,8 +92,9 @@ typedef enum {
   GATTN_PATH_HYBRID = 3  /* per row window: dense windows on the MFMA path, the rest gathered */
 } gattn_path;
 
-#define GATTN_FLAG_VALIDATE 1u /* gattn_forward: copy row_ptr / col_idx to the host and check them
-                                  first (a debugging aid; synchronizes the stream)              */
+#define GATTN_FLAG_VALIDATE 1u /* gattn_forward / gattn_aggregate: check row_ptr, col_idx and
+                                  edge_ids on the device first (BAD_GRAPH; synchronizes the
+                                  stream; allocates nothing)                                   */
 
 /* ------------------------------------------------------------------------ */
 GATTN_API int gattn_abi_version(void);
@@ -207,7 +208,8 @@ typedef struct {
      e[edge_ids[p]] for CSR position p (pass gattn_build_csr's edge_perm to keep
      E in the caller's original edge order).  Values must lie in [0, nnz), and
      form a permutation when e_out is given (two positions writing one row
-     race).  GATTN_FLAG_VALIDATE checks both on the host (GATTN_ERR_BAD_GRAPH);
+     race).  GATTN_FLAG_VALIDATE checks both (GATTN_ERR_BAD_GRAPH; the range on
+     the device, the permutation with a host copy of the ids);
      unchecked, an out-of-range id is clamped into range (no fault, the
      result is unspecified).  Read only when e is given.                       */
   const int32_t* edge_ids;

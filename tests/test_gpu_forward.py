@@ -209,6 +209,21 @@ def test_argument_errors(gsa):
     with pytest.raises(gsa.GattnError) as ei:
         gsa.gattn_forward(rp, ci_bad, c.q, c.k, c.v, validate=True)
     assert ei.value.status == gsa.GATTN_ERR_BAD_GRAPH
+    # the device-side check: every kind of malformed CSR, and a valid one passes
+    bad_rps = []
+    r1 = rp.clone(); r1[0] = 1; bad_rps.append(r1)                        # row_ptr[0] != 0
+    r2 = rp.clone(); r2[-1] = r2[-1] - 1; bad_rps.append(r2)              # row_ptr[N] != nnz
+    r3 = rp.clone(); r3[c.n // 2] = r3[c.n // 2 + 1] + 1; bad_rps.append(r3)  # decreasing
+    for r in bad_rps:
+        with pytest.raises(gsa.GattnError) as ei:
+            gsa.gattn_forward(r, ci, c.q, c.k, c.v, validate=True)
+        assert ei.value.status == gsa.GATTN_ERR_BAD_GRAPH
+    ci_neg = ci.clone()
+    ci_neg[-1] = -1
+    with pytest.raises(gsa.GattnError) as ei:
+        gsa.gattn_forward(rp, ci_neg, c.q, c.k, c.v, validate=True)
+    assert ei.value.status == gsa.GATTN_ERR_BAD_GRAPH
+    assert torch.equal(gsa.gattn_forward(rp, ci, c.q, c.k, c.v, validate=True), gsa.gattn_forward(rp, ci, c.q, c.k, c.v))
     # without validation a bad index is clamped: wrong numbers, no fault
     out = gsa.gattn_forward(rp, ci_bad, c.q, c.k, c.v)
     torch.cuda.synchronize()
