@@ -9,15 +9,17 @@
 //   S^T (16 src x 16 rows) = K_t (16 x D) . Q_w^T (D x 16)
 //        v_mfma_f32_16x16x32_{f16,bf16}, D/32 steps.  Lane l holds
 //        S[row l%16][src 4(l/16)+i], i = 0..3.
-//   masked entries -> -inf; running row max / sum in fp32 (online softmax),
-//        reduced over a row's four 16-lane groups with cross-row lane swaps
+//   masked entries -> -inf; online softmax in fp32 against a per-row
+//        reference max that moves only when a logit passes it by 2^8 (the
+//        row max over a row's four 16-lane groups, by cross-row lane
+//        swaps, runs only then); per-lane partial sums, reduced at the end
 //   O^T (D x 16 rows) += V_t^T (D x 16 src) . P^T (16 src x 16 rows)
 //        v_mfma_f32_16x16x16_{f16,bf16}, D/16 blocks.  The B operand P^T
 //        needs lane l to hold P[row l%16][src 4(l/16)+i] -- exactly the S^T
 //        accumulator layout, so P goes from the SDDMM accumulators to the
 //        SpMM operand without leaving the registers (our counterpart of
-//        Fused3S's register remapping).  V_t^T comes from a per-wave LDS
-//        copy of the tile's V rows through gfx950's transposing LDS read.
+//        Fused3S's register remapping).  K_t and V_t^T come from a per-wave
+//        LDS copy of the tile's rows (V through gfx950's transposing read).
 //   O^T accumulators keep row l%16 in lane l like the softmax state, so the
 //   per-row rescale is a register multiply.
 //
