@@ -95,6 +95,9 @@ def parse():
                    help="also time an eager PyTorch formulation of the same forward (context only)")
     p.add_argument("--ceiling", action="store_true",
                    help="gather rate against the size of the gathered table (graphs shaped like config 4)")
+    p.add_argument("--kv-layout", default="separate", choices=["separate", "interleaved"],
+                   help="K and V as two [N, H, D] tensors, or as the halves of one [N, 2, H, D] buffer "
+                        "(row views with a row stride of 2 H D: a row's K and V bytes adjacent)")
     p.add_argument("--counters-run", action="store_true")
     p.add_argument("--ingest-counters", default=None)
     args = p.parse_args()
@@ -165,12 +168,16 @@ def roofline_basis(n, h, d, s, variant="forward"):
 
 
 class Batch:
-    def __init__(self, wl, dev, host, variant="forward", partition="node"):
+    def __init__(self, wl, dev, host, variant="forward", partition="node", kv_layout="separate"):
         import torch
         import graph_sparse_attention_amd as gsa
         self.src = host["src"].to(dev)
         self.dst = host["dst"].to(dev)
         self.q, self.k, self.v = (host[x].to(dev) for x in ("q", "k", "v"))
+        if kv_layout == "interleaved" and variant != "aggregate":
+            # one [N, 2, H, D] buffer; k and v are its halves (row stride 2 H D)
+            kv = torch.stack((self.k, self.v), dim=1)
+            self.k, self.v = kv[:, 0], kv[:, 1]
         self.e = host["e"].to(dev) if host["e"] is not None else None
         self.out = torch.empty_like(self.q)
         self.w = host["w"].to(dev) if host.get("w") is not None else None
@@ -370,13 +377,14 @@ def eager_context(torch, wl, b, fwd_ms_median, reps=20):
 # counters
 # ---------------------------------------------------------------------------
 
-def counters_file(path_key, config, variant="forward", partition="node"):
-    suffix = ("" if variant == "forward" else f"_{variant}") + ("_balanced" if partition == "balanced" and path_key == "gather" else "")
+def counters_file(path_key, config, variant="forward", partition="node", kv_layout="separate"):
+    suffix = (("" if variant == "forward" else f"_{variant}") + ("_balanced" if partition == "balanced" and path_key == "gather" else "")
+              + ("_kv_interleaved" if kv_layout == "interleaved" else ""))
     return os.path.join(PROFILES, f"forward_{path_key}_config{config}{suffix}_counters.json")
 
 
-def load_traffic(path_key, config, variant="forward", partition="node"):
-    f = counters_file(path_key, config, variant, partition)
+def load_traffic(path_key, config, variant="forward", partition="node", kv_layout="separate"):
+    f = counters_file(path_key, config, variant, partition, kv_layout)
     if not os.path.exists(f):
         return None
     d = json.load(open(f))
@@ -385,19 +393,20 @@ def load_traffic(path_key, config, variant="forward", partition="node"):
     return d
 
 
-def counter_commands(dirname, config, path_key, variant, partition):
+def counter_commands(dirname, config, path_key, variant, partition, kv_layout="separate"):
     """The runs behind a counter file: from /tmp with TMPDIR=/tmp, R = the
     repository root, one run per counter, the CSVs under DIR/FETCH and
     DIR/WRITE, then the ingestion from the repository root."""
     args = (f"--config {config} --path {path_key}" + (f" --variant {variant}" if variant != "forward" else "")
-            + (" --partition balanced" if partition == "balanced" and path_key == "gather" else ""))
+            + (" --partition balanced" if partition == "balanced" and path_key == "gather" else "")
+            + (" --kv-layout interleaved" if kv_layout == "interleaved" else ""))
     rel = os.path.relpath(os.path.abspath(dirname), ROOT)
     return ([f"rocprofv3 --pmc {ctr} -d $R/{rel}/{ctr.split('_')[0]} -o run --output-format csv -- "
              f"python3 -u $R/bench.py {args} --counters-run" for ctr in ("FETCH_SIZE", "WRITE_SIZE")]
             + [f"python3 bench.py {args} --ingest-counters {rel}"])
 
 
-def ingest_counters(dirname, config, path_key, variant="forward", partition="node"):
+def ingest_counters(dirname, config, path_key, variant="forward", partition="node", kv_layout="separate"):
     """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the forward kernel
     and of the calibration copy; scale by the copy's bytes-per-count."""
     rows = []
@@ -432,15 +441,16 @@ def ingest_counters(dirname, config, path_key, variant="forward", partition="nod
     fr = COPY_BYTES / (copy_read * 1024.0) if copy_read else None
     fw = COPY_BYTES / (copy_write * 1024.0) if copy_write else None
     out = {"kernel": kern, "config": config, "variant": variant, "partition": partition if path_key == "gather" else None,
+           "kv_layout": kv_layout,
            "kernel_source_sha256_16": src_hash(path_key),
            "fetch_kib_per_dispatch": res.get("fwd_FETCH_SIZE"), "write_kib_per_dispatch": res.get("fwd_WRITE_SIZE"),
            "copy_fetch_kib": copy_read, "copy_write_kib": copy_write, "copy_bytes_each_way": COPY_BYTES,
            "read_scale": fr, "write_scale": fw,
-           "commands": counter_commands(dirname, config, path_key, variant, partition)}
+           "commands": counter_commands(dirname, config, path_key, variant, partition, kv_layout)}
     if res.get("fwd_FETCH_SIZE") is not None and fr and res.get("fwd_WRITE_SIZE") is not None and fw:
         out["hbm_bytes_per_launch"] = res["fwd_FETCH_SIZE"] * 1024.0 * fr + res["fwd_WRITE_SIZE"] * 1024.0 * fw
     os.makedirs(PROFILES, exist_ok=True)
-    with open(counters_file(path_key, config, variant, partition), "w") as fh:
+    with open(counters_file(path_key, config, variant, partition, kv_layout), "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out))
 
@@ -505,7 +515,7 @@ def main():
     import workloads as W
     if args.ingest_counters:
         path_key = args.path if args.path in ("mfma", "hybrid") else "gather"
-        ingest_counters(args.ingest_counters, args.config, path_key, args.variant, args.partition)
+        ingest_counters(args.ingest_counters, args.config, path_key, args.variant, args.partition, args.kv_layout)
         return
 
     import torch
@@ -548,7 +558,7 @@ def main():
         torch.cuda.synchronize()
         b.copy_(a)                      # calibration: COPY_BYTES read + COPY_BYTES written (runtime copyBuffer kernel)
         torch.cuda.synchronize()
-        bt = Batch(wl, dev, host, args.variant, args.partition)
+        bt = Batch(wl, dev, host, args.variant, args.partition, args.kv_layout)
         rp, ci, pe = bt.csr(bt.src, bt.dst)
         if use_rw:
             plans(bt, rp, ci)
@@ -561,7 +571,7 @@ def main():
     # R rotating copies so that one step's inputs are not cache-resident
     R = max(2, min(16, math.ceil(3 * MALL_BYTES / max(batch_bytes(wl, es, args.variant), 1)) + 1))
     print(f"# {wl.name}: N={wl.num_nodes} nnz={wl.nnz}; {R} rotating batches", file=sys.stderr, flush=True)
-    batches = [Batch(wl, dev, host, args.variant, args.partition) for _ in range(R)]
+    batches = [Batch(wl, dev, host, args.variant, args.partition, args.kv_layout) for _ in range(R)]
     for b in batches:               # each batch's CSR once (rebuilt per step with --include-build)
         b.csr(b.src, b.dst)
         if use_rw:
@@ -680,7 +690,7 @@ def main():
     balg = bgat if basis == "gather" else bmin
     achieved = balg / (fwd_ms * 1e-3) / 1e9
     pk = path if path in ("mfma", "hybrid") else "gather"
-    tr = load_traffic(pk, args.config, args.variant, args.partition)
+    tr = load_traffic(pk, args.config, args.variant, args.partition, args.kv_layout)
     traffic = round(tr["hbm_bytes_per_launch"]) if tr and tr.get("hbm_bytes_per_launch") else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -710,6 +720,7 @@ def main():
                       "pipeline": ("CSR build of batch i+1 on a second stream during the forward of batch i"
                                    if side is not None else None),
                       "partition": args.partition if path == "gather" else None,
+                      "kv_layout": args.kv_layout if args.variant != "aggregate" else None,
                       "forward_path": path,
                       "rotating_batches": R},
            "roofline": roofline,

@@ -75,7 +75,7 @@ class _ForwardArgs(ctypes.Structure):
                 ("eps", ctypes.c_float), ("path", ctypes.c_int), ("rw", ctypes.POINTER(_RowWindows)),
                 ("flags", ctypes.c_uint32), ("edge_ids", ctypes.c_void_p), ("e_out", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("hybrid", ctypes.POINTER(_Hybrid))]
+                ("hybrid", ctypes.POINTER(_Hybrid)), ("q_stride", ctypes.c_int64), ("kv_stride", ctypes.c_int64)]
 
 
 class _AggregateArgs(ctypes.Structure):
@@ -331,6 +331,8 @@ def _forward_args(row_ptr, col_idx, q, k, v, e, out, mode, scale, clip, eps, pat
     a.flags = GATTN_FLAG_VALIDATE if validate else 0
     a.edge_ids = None if edge_ids is None else edge_ids.data_ptr()
     a.e_out = None if e_out is None else e_out.data_ptr()
+    a.q_stride = _row_stride(q)
+    a.kv_stride = _row_stride(k)
     return a, keep
 
 
@@ -382,6 +384,25 @@ def _check_node_tensor(t, name, like):
         raise ValueError(f"{name} must match q in dtype, shape and device and be contiguous")
 
 
+def _row_stride(t):
+    """Row stride of an [N, H, D] tensor for the C ABI: 0 when its rows are
+    packed, else the stride of dim 0 in elements."""
+    N, H, D = t.shape
+    return 0 if t.stride(0) == H * D or N <= 1 else t.stride(0)
+
+
+def _check_rows(t, name, like):
+    """An [N, H, D] view whose rows may be strided (a fused projection's
+    output): each row's H x D block packed, the row stride a multiple of 8
+    elements, at least H x D."""
+    if t.dim() != 3 or t.dtype != like.dtype or t.shape != like.shape or not t.is_cuda or t.device != like.device:
+        raise ValueError(f"{name} must be an [N, H, D] GPU tensor matching q in dtype, shape and device")
+    N, H, D = t.shape
+    if t.stride(2) != 1 or (H > 1 and t.stride(1) != D) or (N > 1 and (t.stride(0) < H * D or t.stride(0) % 8)):
+        raise ValueError(f"{name}: each row's [H, D] block must be packed and the row stride a multiple of 8 "
+                         "elements, at least H * D")
+
+
 def gattn_forward(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                   e: Optional[torch.Tensor] = None, mode: str = "standard", scale: Optional[float] = None,
                   clip=(-5.0, 5.0), eps: float = 1e-6, path: str = "auto", rw: Optional[RowWindows] = None,
@@ -398,10 +419,13 @@ def gattn_forward(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch.Tensor,
     workgroups: for graphs whose hubs hold many times a workgroup's share).
     hybrid (with rw): a gattn_build_hybrid plan for path "hybrid" (or
     "auto"): dense row windows on the MFMA path, the other rows gathered."""
-    if q.dim() != 3 or not q.is_contiguous() or not q.is_cuda or q.dtype not in _DTYPES:
-        raise ValueError("q must be a contiguous [N, H, D] GPU tensor")
-    _check_node_tensor(k, "k", q)
-    _check_node_tensor(v, "v", q)
+    if q.dim() != 3 or not q.is_cuda or q.dtype not in _DTYPES:
+        raise ValueError("q must be an [N, H, D] GPU tensor")
+    _check_rows(q, "q", q)
+    _check_rows(k, "k", q)
+    _check_rows(v, "v", q)
+    if _row_stride(k) != _row_stride(v):
+        raise ValueError("k and v must have the same row stride")
     N, H, D = q.shape
     row_ptr, col_idx = _csr(row_ptr, col_idx, N, q.device)
     if e is not None and (e.dtype != q.dtype or tuple(e.shape) != (col_idx.numel(), H, D) or not e.is_contiguous()
@@ -422,7 +446,7 @@ def gattn_forward(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch.Tensor,
     if rw is not None and rw.num_nodes != N:
         raise ValueError(f"rw was built for {rw.num_nodes} nodes, q has {N}")
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     else:
         _check_node_tensor(out, "out", q)
     a, keep = _forward_args(row_ptr, col_idx, q, k, v, e, out, mode, scale, clip, eps, path, rw, validate,
@@ -446,10 +470,13 @@ def gattn_forward_noalloc(row_ptr: torch.Tensor, col_idx: torch.Tensor, q: torch
     Calls whose executions overlap on one GPU race on the scratch array."""
     if out is None:
         raise ValueError("gattn_forward_noalloc writes into a given `out`")
-    if q.dim() != 3 or not q.is_contiguous() or not q.is_cuda or q.dtype not in _DTYPES:
-        raise ValueError("q must be a contiguous [N, H, D] GPU tensor")
-    for name, t in (("k", k), ("v", v), ("out", out)):
-        _check_node_tensor(t, name, q)
+    if q.dim() != 3 or not q.is_cuda or q.dtype not in _DTYPES:
+        raise ValueError("q must be an [N, H, D] GPU tensor")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_rows(t, name, q)
+    if _row_stride(k) != _row_stride(v):
+        raise ValueError("k and v must have the same row stride")
+    _check_node_tensor(out, "out", q)
     N, H, D = q.shape
     row_ptr, col_idx = _csr(row_ptr, col_idx, N, q.device)
     nnz = col_idx.numel()

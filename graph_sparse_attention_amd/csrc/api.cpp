@@ -13,7 +13,7 @@
 using namespace gattn;
 
 // the Python binding mirrors these layouts with ctypes
-static_assert(sizeof(gattn_forward_args) == 168, "gattn_forward_args layout");
+static_assert(sizeof(gattn_forward_args) == 184, "gattn_forward_args layout");
 static_assert(sizeof(gattn_hybrid) == 32, "gattn_hybrid layout");
 static_assert(sizeof(gattn_aggregate_args) == 104, "gattn_aggregate_args layout");
 static_assert(sizeof(gattn_rowwindows) == 40, "gattn_rowwindows layout");
@@ -75,15 +75,22 @@ gattn_status check_forward(const gattn_forward_args* a, bool launch) {
   const void* t[] = {a->q, a->k, a->v, a->e, a->out, a->e_out};
   for (const void* p : t)
     if (!aligned(p, 16)) return GATTN_ERR_INVALID_VALUE;
-  const size_t node_bytes = (size_t)a->num_nodes * a->num_heads * a->head_dim * elem_size(a->dtype);
+  const int64_t hd = (int64_t)a->num_heads * a->head_dim;
+  for (int64_t st : {a->q_stride, a->kv_stride})
+    if (st != 0 && (st < hd || st % 8 != 0 || st > ((int64_t)1 << 24))) return GATTN_ERR_INVALID_VALUE;
+  const size_t es = elem_size(a->dtype);
+  const size_t node_bytes = (size_t)a->num_nodes * hd * es;
+  // bytes a strided [N, H, D] view spans: from row 0 to the end of row N - 1
+  auto span = [&](int64_t st) { return ((size_t)(a->num_nodes - 1) * (size_t)(st ? st : hd) + (size_t)hd) * es; };
+  const size_t q_bytes = span(a->q_stride), kv_bytes = span(a->kv_stride);
   const size_t edge_bytes = (size_t)a->nnz * a->num_heads * a->head_dim * elem_size(a->dtype);
-  if (overlap(a->out, node_bytes, a->q, node_bytes) || overlap(a->out, node_bytes, a->k, node_bytes) ||
-      overlap(a->out, node_bytes, a->v, node_bytes) || overlap(a->out, node_bytes, a->e, edge_bytes))
+  if (overlap(a->out, node_bytes, a->q, q_bytes) || overlap(a->out, node_bytes, a->k, kv_bytes) ||
+      overlap(a->out, node_bytes, a->v, kv_bytes) || overlap(a->out, node_bytes, a->e, edge_bytes))
     return GATTN_ERR_INVALID_VALUE;
   if (a->e_out && a->nnz > 0) {
     const size_t ib = (size_t)a->nnz * 4;
-    if (overlap(a->e_out, edge_bytes, a->q, node_bytes) || overlap(a->e_out, edge_bytes, a->k, node_bytes) ||
-        overlap(a->e_out, edge_bytes, a->v, node_bytes) || overlap(a->e_out, edge_bytes, a->e, edge_bytes) ||
+    if (overlap(a->e_out, edge_bytes, a->q, q_bytes) || overlap(a->e_out, edge_bytes, a->k, kv_bytes) ||
+        overlap(a->e_out, edge_bytes, a->v, kv_bytes) || overlap(a->e_out, edge_bytes, a->e, edge_bytes) ||
         overlap(a->e_out, edge_bytes, a->out, node_bytes) || overlap(a->e_out, edge_bytes, a->row_ptr, 4 * ((size_t)a->num_nodes + 1)) ||
         overlap(a->e_out, edge_bytes, a->col_idx, ib) || overlap(a->e_out, edge_bytes, a->edge_ids, ib))
       return GATTN_ERR_INVALID_VALUE;
@@ -91,8 +98,8 @@ gattn_status check_forward(const gattn_forward_args* a, bool launch) {
   if (a->workspace) {
     const size_t wb = a->workspace_bytes;
     if (!aligned(a->workspace, 256)) return GATTN_ERR_INVALID_VALUE;
-    if (overlap(a->workspace, wb, a->q, node_bytes) || overlap(a->workspace, wb, a->k, node_bytes) ||
-        overlap(a->workspace, wb, a->v, node_bytes) || overlap(a->workspace, wb, a->e, edge_bytes) ||
+    if (overlap(a->workspace, wb, a->q, q_bytes) || overlap(a->workspace, wb, a->k, kv_bytes) ||
+        overlap(a->workspace, wb, a->v, kv_bytes) || overlap(a->workspace, wb, a->e, edge_bytes) ||
         overlap(a->workspace, wb, a->out, node_bytes) || overlap(a->workspace, wb, a->e_out, edge_bytes) ||
         overlap(a->workspace, wb, a->row_ptr, 4 * ((size_t)a->num_nodes + 1)) ||
         overlap(a->workspace, wb, a->col_idx, (size_t)a->nnz * 4) ||

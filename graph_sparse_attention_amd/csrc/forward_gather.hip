@@ -215,6 +215,9 @@ GatherArgs forward_gather_args(const gattn_forward_args& a) {
   ga.nnz = a.nnz;
   ga.n = a.num_nodes;
   ga.H = a.num_heads;
+  const int64_t hd = (int64_t)a.num_heads * a.head_dim;
+  ga.q_stride = a.q_stride ? a.q_stride : hd;
+  ga.kv_stride = a.kv_stride ? a.kv_stride : hd;
   ga.scale = a.mode == GATTN_SOFTMAX_STANDARD ? a.scale * kLog2e : a.scale;
   ga.lo = a.clip_lo;
   ga.hi = a.clip_hi;
@@ -257,6 +260,7 @@ hipError_t launch_aggregate_gather(const gattn_aggregate_args& a, hipStream_t s)
   ga.nnz = a.nnz;
   ga.n = a.num_nodes;
   ga.H = a.num_heads;
+  ga.q_stride = ga.kv_stride = (int64_t)a.num_heads * a.head_dim;
   ga.eps = a.eps;
   ga.ids = a.edge_ids;
   ga.w = a.w;

@@ -54,7 +54,9 @@ struct MfmaArgs {
   int32_t n, H, W;
   int32_t nwb;        // windows in the grid (W, or the hybrid plan's dense ones)
   float scale_l2;     // scale * log2(e)
-  uint32_t kv_bytes;  // bytes of K (and of V), at most 2^31
+  uint32_t kv_bytes;  // bytes K (and V) span, at most 2^31
+  uint32_t q_bytes;   // bytes Q spans, at most 2^31
+  int64_t q_stride, kv_stride;  // row strides (elements) of Q and of K / V
 };
 
 template <bool BF16>
@@ -164,11 +166,11 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
   constexpr int RPI = 64 / CPR;  // rows per 64-lane load or store
   {
     const __amdgpu_buffer_rsrc_t rq =
-        __builtin_amdgcn_make_buffer_rsrc((void*)a.q, (short)0, (int)a.kv_bytes, kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.q, (short)0, (int)a.q_bytes, kBufferWord3);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int row = s * RPI + lane / CPR;
-      const uint32_t off = (uint32_t)((((uint64_t)(16 * w + row) * rowstride + (uint64_t)h * D) * 2)) + 16 * (lane % CPR);
+      const uint32_t off = (uint32_t)((((uint64_t)(16 * w + row) * a.q_stride + (uint64_t)h * D) * 2)) + 16 * (lane % CPR);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)&s_v[wave][1][s * 1024],
                                                16, off, 0, 0, 0);
     }
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(kWavesPerWg * 64, 2) void mfma_kernel(MfmaArgs a) {
       const int row = s * RPI + lane / CPR;
       const int32_t col = s_col[wave][c + row];
       const uint32_t off = (uint32_t)col < (uint32_t)a.n
-                               ? (uint32_t)(((uint64_t)col * rowstride + (uint64_t)h * D) * 2) +
+                               ? (uint32_t)(((uint64_t)col * a.kv_stride + (uint64_t)h * D) * 2) +
                                      16 * ((lane % CPR) ^ (row % CPR))
                                : kPastEnd;
       dma16(dk, off, &s_k[wave][b][s * 1024]);
@@ -397,10 +399,20 @@ hipError_t launch_b(const gattn_forward_args& fa, const MfmaArgs& ma, int32_t bl
 
 }  // namespace
 
+namespace {
+// bytes a 16-bit [N, H, D] view with row stride st (0: packed) spans
+uint64_t span_bytes(const gattn_forward_args& a, int64_t st) {
+  const uint64_t hd = (uint64_t)a.num_heads * a.head_dim;
+  if (a.num_nodes <= 0) return 0;
+  return ((uint64_t)(a.num_nodes - 1) * (st ? (uint64_t)st : hd) + hd) * 2;
+}
+}  // namespace
+
 bool mfma_supported(const gattn_forward_args& a) {
-  const uint64_t kv_bytes = (uint64_t)a.num_nodes * a.num_heads * a.head_dim * 2;
+  // K, V and Q are read through 32-bit buffer offsets, padding columns at 2^31
   return (a.dtype == GATTN_F16 || a.dtype == GATTN_BF16) && a.mode == GATTN_SOFTMAX_STANDARD && a.e == nullptr &&
-         (a.head_dim == 32 || a.head_dim == 64 || a.head_dim == 128) && kv_bytes <= ((uint64_t)1 << 31);
+         (a.head_dim == 32 || a.head_dim == 64 || a.head_dim == 128) &&
+         span_bytes(a, a.kv_stride) <= ((uint64_t)1 << 31) && span_bytes(a, a.q_stride) <= ((uint64_t)1 << 31);
 }
 
 hipError_t launch_forward_mfma(const gattn_forward_args& fa, const int32_t* windows, int32_t num_windows,
@@ -420,7 +432,11 @@ hipError_t launch_forward_mfma(const gattn_forward_args& fa, const int32_t* wind
   ma.H = fa.num_heads;
   ma.W = fa.rw->num_windows;
   ma.scale_l2 = fa.scale * kLog2e;
-  ma.kv_bytes = (uint32_t)((uint64_t)fa.num_nodes * fa.num_heads * fa.head_dim * 2);
+  ma.kv_bytes = (uint32_t)span_bytes(fa, fa.kv_stride);
+  ma.q_bytes = (uint32_t)span_bytes(fa, fa.q_stride);
+  const int64_t hd = (int64_t)fa.num_heads * fa.head_dim;
+  ma.q_stride = fa.q_stride ? fa.q_stride : hd;
+  ma.kv_stride = fa.kv_stride ? fa.kv_stride : hd;
   const int32_t blocks = windows ? num_windows : ma.W;
   ma.nwb = blocks;
   return fa.dtype == GATTN_BF16 ? launch_b<true>(fa, ma, blocks, s) : launch_b<false>(fa, ma, blocks, s);

@@ -115,6 +115,7 @@ struct GatherArgs {
   const uint8_t* __restrict__ e;
   uint8_t* __restrict__ out;
   int64_t nnz;
+  int64_t q_stride, kv_stride;  // row strides (elements) of q and of k / v
   int32_t n, H, HB, log2G, npw;
   float scale;  // standard: scale * log2(e); clipped: scale
   float lo, hi, eps;
@@ -378,10 +379,14 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
   // and this lane's 16 bytes sit at lane_b inside it (0 for idle lanes, whose
   // loads are issued like the others and never used).
   const uint32_t rowbytes = (uint32_t)(rowstride * ESZ);
+  const uint32_t kv_rowbytes = (uint32_t)(a.kv_stride * ESZ);  // K and V rows may be strided
   const uint64_t lane_b = active ? (uint64_t)eoff * ESZ : 0;
   const int hw = active ? head : 0;
   auto row_ptr16 = [&](const uint8_t* base, int row) -> const uint8_t* {
     return base + lane_b + (uint64_t)(uint32_t)row * rowbytes;
+  };
+  auto kv_ptr16 = [&](const uint8_t* base, int row) -> const uint8_t* {
+    return base + lane_b + (uint64_t)(uint32_t)row * kv_rowbytes;
   };
   auto load_e = [&](int row) -> u32x4 {
     const uint8_t* ptr = row_ptr16(a.e, row);
@@ -440,7 +445,7 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
   const int qn = AGG ? 0 : min(nn, qcap) * chunks;
   auto q_src = [&](int t) {
     const int li = t / chunks, c = t - li * chunks;
-    return a.q + ((int64_t)(n0 + li) * rowstride + (int64_t)hb * a.HB * D + c * VEC) * ESZ;
+    return a.q + ((int64_t)(n0 + li) * a.q_stride + (int64_t)hb * a.HB * D + c * VEC) * ESZ;
   };
   auto q_dst = [&](int t) {
     const int li = t / chunks, c = t - li * chunks;
@@ -506,7 +511,7 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
       if (nd < qcap) {
         Conv<T>::widen(*reinterpret_cast<const u32x4*>(s_q + nd * qrow + lig * 16), qf);
       } else {
-        Conv<T>::widen(ld16(a.q + ((int64_t)(n0 + nd) * rowstride + eoff) * ESZ), qf);
+        Conv<T>::widen(ld16(a.q + ((int64_t)(n0 + nd) * a.q_stride + eoff) * ESZ), qf);
       }
     }
   };
@@ -571,8 +576,8 @@ __global__ __launch_bounds__(kGatherThreads, GATTN_GATHER_MIN_WAVES) void gather
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         kr[u] = u32x4{0u, 0u, 0u, 0u};
-        if constexpr (!AGG) kr[u] = ld16(row_ptr16(a.k, cols[u]));
-        vr[u] = ld16(row_ptr16(a.v, cols[u]));
+        if constexpr (!AGG) kr[u] = ld16(kv_ptr16(a.k, cols[u]));
+        vr[u] = ld16(kv_ptr16(a.v, cols[u]));
       }
       // the next step's indices and edge rows, in flight while this one computes
 #pragma unroll

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define GATTN_ABI_VERSION 4
+#define GATTN_ABI_VERSION 5
 
 #ifndef GATTN_API
 #define GATTN_API __attribute__((visibility("default")))
@@ -235,6 +235,14 @@ typedef struct {
      by gattn_build_hybrid for this graph, these row windows and this geometry
      (H, D, dtype, mode, e).  Nullable; required by GATTN_PATH_HYBRID.          */
   const gattn_hybrid* hybrid;
+  /* Row strides, in elements, of q and of k / v (k and v share one): 0 means
+     num_heads * head_dim (rows packed).  Otherwise at least that and a
+     multiple of 8 elements (16 bytes), so that q, k and v may be views into a
+     fused projection's output; k and v interleaved in one [N, 2, H, D] buffer
+     (kv_stride = 2 H D) put an edge's K and V rows side by side, which random
+     row gathers read faster.  out, e and e_out are always packed.              */
+  int64_t q_stride;
+  int64_t kv_stride;
 } gattn_forward_args;
 
 /* out[i, h, :] = sum_p alpha_p(h) v[col_idx[p], h, :] over the in-edges p of i;

@@ -46,10 +46,10 @@ def test_enums_and_strings(gsa):
                  "GATTN_ERR_DUPLICATE_EDGE", "GATTN_ERR_BUFFER_TOO_SMALL", "GATTN_ERR_HIP"]:
         m = re.search(name + r"\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(gsa, name)
-    assert gsa.gattn_abi_version() == 4
+    assert gsa.gattn_abi_version() == 5
     assert gsa.gattn_status_string(gsa.GATTN_ERR_DUPLICATE_EDGE).startswith("repeated")
     assert gsa.gattn_status_string(99) == "unknown status"
-    assert ctypes.sizeof(gsa._ForwardArgs) == 168
+    assert ctypes.sizeof(gsa._ForwardArgs) == 184
     assert ctypes.sizeof(gsa._Hybrid) == 32
     assert ctypes.sizeof(gsa._AggregateArgs) == 104
 
@@ -107,6 +107,12 @@ def test_forward_argument_errors(gsa):
         (dict(e_out=(1 << 32) + (16 << 20) + 8, e=(1 << 32) + (14 << 20), mode=gsa.GATTN_SOFTMAX_CLIPPED),
          gsa.GATTN_ERR_INVALID_VALUE),                                 # misaligned
         (dict(edge_ids=(1 << 32) + 2), gsa.GATTN_ERR_INVALID_VALUE),   # misaligned
+        # row strides of q and of k / v: at least H * D, multiples of 8, at most 2^24
+        (dict(q_stride=256), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(kv_stride=516), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(kv_stride=(1 << 24) + 8), gsa.GATTN_ERR_INVALID_VALUE),
+        (dict(q_stride=1024, out=(1 << 32) + (2 << 20) + 102400), gsa.GATTN_ERR_INVALID_VALUE),  # in q's span
+        (dict(kv_stride=2048, out=(1 << 32) + (6 << 20) + 102400), gsa.GATTN_ERR_INVALID_VALUE),  # in v's span
         (dict(workspace=(1 << 32) + (20 << 20) + 64, workspace_bytes=4096), gsa.GATTN_ERR_INVALID_VALUE),
         (dict(workspace=(1 << 32) + (8 << 20), workspace_bytes=4096), gsa.GATTN_ERR_INVALID_VALUE),  # aliases out
     ]
@@ -114,6 +120,24 @@ def test_forward_argument_errors(gsa):
         a = fake_args(gsa, **kw)
         assert L.gattn_forward(ctypes.byref(a), None) == want, kw
     assert L.gattn_forward(None, None) == gsa.GATTN_ERR_INVALID_VALUE
+
+
+def test_strided_rows_accepted(gsa):
+    # strided q / k / v pass the host checks (out just past q's packed rows is
+    # fine while q is packed); the MFMA path needs the strided spans under 2^31
+    a = fake_args(gsa, out=(1 << 32) + (2 << 20) + 102400, q_stride=0, kv_stride=1024)
+    assert path_of(gsa, a)[0] == gsa.GATTN_OK
+    rw = gsa._RowWindows(7, 16 * 10, (1 << 32) + (10 << 20), (1 << 32) + (11 << 20), (1 << 32) + (12 << 20))
+    a = fake_args(gsa, kv_stride=1024, path=gsa.GATTN_PATH_MFMA)
+    a.rw = ctypes.pointer(rw)
+    assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_MFMA)
+    # 2^17 rows 2^15 bytes apart: K and V each span (2^17 - 1) * 2^15 + 1024 bytes > 2^31
+    a.num_nodes, a.kv_stride = 1 << 17, 1 << 14
+    a.k, a.v, a.out = (1 << 40), (1 << 41), (1 << 39)
+    a.rw.contents.num_windows = (1 << 17) // 16
+    assert path_of(gsa, a)[0] == gsa.GATTN_ERR_UNSUPPORTED
+    a.path = gsa.GATTN_PATH_AUTO
+    assert path_of(gsa, a) == (gsa.GATTN_OK, gsa.GATTN_PATH_GATHER)
 
 
 def test_path_resolution(gsa):
