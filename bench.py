@@ -9,7 +9,10 @@ the gattn-triton article builds its CSC index outside the timed kernel.
 ``--include-build`` times gattn_build_csr + gattn_forward per step instead.
 The default workload is the largest configuration that fits one GPU: the
 power-law graph of 2.45M destinations and 101M edges (lognormal in-degree,
-uniform sources), one head of 64, bf16, standard softmax.
+uniform sources), one head of 64, bf16, standard softmax.  K and V sit in
+one [N, 2, H, D] buffer, as a layer's fused K|V projection writes them
+(``--kv-layout separate`` gives two packed tensors instead); the op reads them
+as two row views, and the gathered bytes per edge are the same either way.
 
 Honest HBM numbers: the step cycles through R copies of the batch whose
 total size is well above the 256 MB Infinity Cache, so every step streams
@@ -95,9 +98,10 @@ def parse():
                    help="also time an eager PyTorch formulation of the same forward (context only)")
     p.add_argument("--ceiling", action="store_true",
                    help="gather rate against the size of the gathered table (graphs shaped like config 4)")
-    p.add_argument("--kv-layout", default="separate", choices=["separate", "interleaved"],
-                   help="K and V as two [N, H, D] tensors, or as the halves of one [N, 2, H, D] buffer "
-                        "(row views with a row stride of 2 H D: a row's K and V bytes adjacent)")
+    p.add_argument("--kv-layout", default="interleaved", choices=["separate", "interleaved"],
+                   help="K and V as the halves of one [N, 2, H, D] buffer, as one fused K|V projection "
+                        "writes them (row views with a row stride of 2 H D: a row's K and V bytes adjacent), "
+                        "or as two packed [N, H, D] tensors")
     p.add_argument("--counters-run", action="store_true")
     p.add_argument("--ingest-counters", default=None)
     args = p.parse_args()
@@ -168,7 +172,7 @@ def roofline_basis(n, h, d, s, variant="forward"):
 
 
 class Batch:
-    def __init__(self, wl, dev, host, variant="forward", partition="node", kv_layout="separate"):
+    def __init__(self, wl, dev, host, variant="forward", partition="node", kv_layout="interleaved"):
         import torch
         import graph_sparse_attention_amd as gsa
         self.src = host["src"].to(dev)
@@ -377,13 +381,13 @@ def eager_context(torch, wl, b, fwd_ms_median, reps=20):
 # counters
 # ---------------------------------------------------------------------------
 
-def counters_file(path_key, config, variant="forward", partition="node", kv_layout="separate"):
+def counters_file(path_key, config, variant="forward", partition="node", kv_layout="interleaved"):
     suffix = (("" if variant == "forward" else f"_{variant}") + ("_balanced" if partition == "balanced" and path_key == "gather" else "")
-              + ("_kv_interleaved" if kv_layout == "interleaved" else ""))
+              + ("_kv_separate" if kv_layout == "separate" else ""))
     return os.path.join(PROFILES, f"forward_{path_key}_config{config}{suffix}_counters.json")
 
 
-def load_traffic(path_key, config, variant="forward", partition="node", kv_layout="separate"):
+def load_traffic(path_key, config, variant="forward", partition="node", kv_layout="interleaved"):
     f = counters_file(path_key, config, variant, partition, kv_layout)
     if not os.path.exists(f):
         return None
@@ -393,20 +397,20 @@ def load_traffic(path_key, config, variant="forward", partition="node", kv_layou
     return d
 
 
-def counter_commands(dirname, config, path_key, variant, partition, kv_layout="separate"):
+def counter_commands(dirname, config, path_key, variant, partition, kv_layout="interleaved"):
     """The runs behind a counter file: from /tmp with TMPDIR=/tmp, R = the
     repository root, one run per counter, the CSVs under DIR/FETCH and
     DIR/WRITE, then the ingestion from the repository root."""
     args = (f"--config {config} --path {path_key}" + (f" --variant {variant}" if variant != "forward" else "")
             + (" --partition balanced" if partition == "balanced" and path_key == "gather" else "")
-            + (" --kv-layout interleaved" if kv_layout == "interleaved" else ""))
+            + (" --kv-layout separate" if kv_layout == "separate" else ""))
     rel = os.path.relpath(os.path.abspath(dirname), ROOT)
     return ([f"rocprofv3 --pmc {ctr} -d $R/{rel}/{ctr.split('_')[0]} -o run --output-format csv -- "
              f"python3 -u $R/bench.py {args} --counters-run" for ctr in ("FETCH_SIZE", "WRITE_SIZE")]
             + [f"python3 bench.py {args} --ingest-counters {rel}"])
 
 
-def ingest_counters(dirname, config, path_key, variant="forward", partition="node", kv_layout="separate"):
+def ingest_counters(dirname, config, path_key, variant="forward", partition="node", kv_layout="interleaved"):
     """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the forward kernel
     and of the calibration copy; scale by the copy's bytes-per-count."""
     rows = []

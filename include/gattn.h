@@ -188,9 +188,9 @@ typedef struct {
   int64_t nnz;                 /* edges; row_ptr[N] must equal it                    */
   const int32_t* row_ptr;      /* [N+1] CSR by destination                           */
   const int32_t* col_idx;      /* [nnz] source per position, any order inside a row  */
-  const void* q;               /* [N, H, D] contiguous, `dtype`, 16-byte aligned     */
-  const void* k;               /* [N, H, D]                                          */
-  const void* v;               /* [N, H, D]                                          */
+  const void* q;               /* [N, H, D] `dtype`, 16-byte aligned; rows q_stride apart */
+  const void* k;               /* [N, H, D], rows kv_stride apart                    */
+  const void* v;               /* [N, H, D], rows kv_stride apart                    */
   const void* e;               /* nullable; [nnz, H, D] by CSR position (or edge_ids) */
   void* out;                   /* [N, H, D] `dtype`; must not alias the inputs       */
   gattn_dtype dtype;           /* of q, k, v, e and out; arithmetic is fp32          */
@@ -240,7 +240,11 @@ typedef struct {
      multiple of 8 elements (16 bytes), so that q, k and v may be views into a
      fused projection's output; k and v interleaved in one [N, 2, H, D] buffer
      (kv_stride = 2 H D) put an edge's K and V rows side by side, which random
-     row gathers read faster.  out, e and e_out are always packed.              */
+     row gathers read faster.  At most 2^24; GATTN_ERR_INVALID_VALUE for a
+     stride outside these rules.  Overlap checks take the strided spans
+     ((N - 1) * stride + H * D elements).  The MFMA path needs each span under
+     2^31 bytes (GATTN_ERR_UNSUPPORTED when it is forced; AUTO then gathers).
+     out, e and e_out are always packed.                                        */
   int64_t q_stride;
   int64_t kv_stride;
 } gattn_forward_args;

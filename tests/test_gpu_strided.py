@@ -133,3 +133,14 @@ def test_strided_views_refused(gsa):
         gsa.gattn_forward(rp_t, ci_t, q, kp, kp)
     with pytest.raises(ValueError, match="packed"):
         gsa.gattn_forward(rp_t, ci_t, q.transpose(1, 2).contiguous().transpose(1, 2), k, v)
+
+
+def test_graph_layer_strided_kv(gsa):
+    # the Python graph layer passes strided views through (AUTO path: row windows)
+    h, d = 4, 64
+    n, rp, ci = graph(16, 8)
+    (k, v), (kc, vc) = fused(n, 2, h, d, "bf16", 31)
+    q = W.cast(np.random.default_rng(32).standard_normal((n, h, d), dtype=np.float32), "bf16").cuda()
+    dst = torch.from_numpy(np.repeat(np.arange(n, dtype=np.int32), np.diff(rp)))   # the CSR's edges as COO
+    g = gsa.Graph.from_coo(torch.from_numpy(ci).cuda(), dst.cuda(), n)
+    assert torch.equal(gsa.forward(g, q, k, v), gsa.forward(g, q, kc, vc))
