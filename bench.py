@@ -85,8 +85,10 @@ def parse():
     p.add_argument("--path", default="auto", choices=["auto", "gather", "mfma", "hybrid"])
     p.add_argument("--min-density", type=float, default=0.09, help="hybrid path: tile density of an MFMA window")
     p.add_argument("--variant", default="forward", choices=list(VARIANTS))
-    p.add_argument("--partition", default="node", choices=["balanced", "node"],
-                   help="gather path: edge-balanced workgroups with cut heavy rows (workspace) or equal node counts")
+    p.add_argument("--partition", default="auto", choices=["auto", "balanced", "node"],
+                   help="gather path: edge-balanced workgroups with cut heavy rows (workspace), equal node "
+                        "counts, or auto: the graph layer's rule (balanced when the largest in-degree is above "
+                        "32x the mean on a graph below 2^24 edges)")
     p.add_argument("--include-build", action="store_true",
                    help="a step is gattn_build_csr + the op (default: the op on a CSR built once per batch)")
     p.add_argument("--pipeline", action="store_true",
@@ -196,6 +198,13 @@ class Batch:
                       gsa.gattn_forward_workspace(rp, ci, self.q, self.k, self.v, self.e, wl.mode,
                                                   e_out=self.e_out is not None))
             self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev) if nbytes else None
+
+
+def resolve_partition(wl):
+    """The gather partition the graph layer picks for this workload's graph."""
+    import graph_sparse_attention_amd as gsa
+    max_degree = int(np.bincount(wl.dst, minlength=wl.num_nodes).max()) if wl.nnz else 0
+    return "balanced" if gsa.Graph.skewed_degrees(wl.num_nodes, wl.nnz, max_degree) else "node"
 
 
 def make_host_inputs(wl, variant="forward"):
@@ -402,7 +411,7 @@ def counter_commands(dirname, config, path_key, variant, partition, kv_layout="i
     repository root, one run per counter, the CSVs under DIR/FETCH and
     DIR/WRITE, then the ingestion from the repository root."""
     args = (f"--config {config} --path {path_key}" + (f" --variant {variant}" if variant != "forward" else "")
-            + (" --partition balanced" if partition == "balanced" and path_key == "gather" else "")
+            + (f" --partition {partition}" if path_key == "gather" else "")
             + (" --kv-layout separate" if kv_layout == "separate" else ""))
     rel = os.path.relpath(os.path.abspath(dirname), ROOT)
     return ([f"rocprofv3 --pmc {ctr} -d $R/{rel}/{ctr.split('_')[0]} -o run --output-format csv -- "
@@ -517,6 +526,11 @@ def main():
         ceiling()
         return
     import workloads as W
+    wl = None
+    if args.partition == "auto":
+        print(f"# generating workload config {args.config}", file=sys.stderr, flush=True)
+        wl = W.make(args.config)
+        args.partition = resolve_partition(wl)
     if args.ingest_counters:
         path_key = args.path if args.path in ("mfma", "hybrid") else "gather"
         ingest_counters(args.ingest_counters, args.config, path_key, args.variant, args.partition, args.kv_layout)
@@ -526,8 +540,9 @@ def main():
     import graph_sparse_attention_amd as gsa
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    print(f"# generating workload config {args.config}", file=sys.stderr, flush=True)
-    wl = W.make(args.config)
+    if wl is None:
+        print(f"# generating workload config {args.config}", file=sys.stderr, flush=True)
+        wl = W.make(args.config)
     if args.variant in ("e_out", "edge_ids") and not wl.has_e:
         sys.exit(f"--variant {args.variant} needs a workload with an edge tensor (config 2)")
     if args.variant == "e_out" and wl.mode != "clipped":

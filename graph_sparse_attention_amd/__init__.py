@@ -579,13 +579,19 @@ class Graph:
 
     def skewed(self) -> bool:
         """Whether hubs would set the gather kernel's end under equal
-        destination counts per workgroup: the largest in-degree is above 32x
+        destination counts per workgroup (Graph.skewed_degrees on this
+        graph's sizes and largest in-degree)."""
+        return Graph.skewed_degrees(self.num_nodes, self.nnz, self.max_degree if self.num_nodes else 0)
+
+    @staticmethod
+    def skewed_degrees(num_nodes: int, nnz: int, max_degree: int) -> bool:
+        """The rule behind Graph.skewed: the largest in-degree is above 32x
         the mean, and the graph is small enough (below 2^24 edges) that its
         workgroups run in few rounds (in many rounds the other workgroups
         absorb a hub's)."""
-        if self.num_nodes == 0 or self.nnz == 0 or self.nnz >= (1 << 24):
+        if num_nodes == 0 or nnz == 0 or nnz >= (1 << 24):
             return False
-        return self.max_degree > 32.0 * self.nnz / self.num_nodes
+        return max_degree > 32.0 * nnz / num_nodes
 
 
 def forward(graph: Graph, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, e: Optional[torch.Tensor] = None,

@@ -367,3 +367,12 @@ def test_noalloc_host_checks(gsa):
     # nothing to compute
     a = fake_args(gsa, num_nodes=0, nnz=0)
     assert L.gattn_forward_noalloc(ctypes.byref(a), None) == gsa.GATTN_OK
+
+
+def test_skewed_degree_rule(gsa):
+    # the graph layer's choice of the balanced gather partition (and bench.py's)
+    rule = gsa.Graph.skewed_degrees
+    assert rule(100, 1000, 321) and not rule(100, 1000, 320)      # above 32x the mean in-degree
+    assert not rule(1 << 20, 1 << 24, 1 << 20)                     # 2^24 edges or more: many rounds
+    assert rule(1 << 20, (1 << 24) - 1, 1 << 20)
+    assert not rule(0, 0, 0) and not rule(10, 0, 0)
