@@ -144,3 +144,28 @@ def test_graph_layer_strided_kv(gsa):
     dst = torch.from_numpy(np.repeat(np.arange(n, dtype=np.int32), np.diff(rp)))   # the CSR's edges as COO
     g = gsa.Graph.from_coo(torch.from_numpy(ci).cuda(), dst.cuda(), n)
     assert torch.equal(gsa.forward(g, q, k, v), gsa.forward(g, q, kc, vc))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_strided_fuzz(gsa, seed):
+    # random geometry, dtype, row padding and path: strided views give the packed copies' bits
+    g = np.random.default_rng(1000 + seed)
+    h, d = [(1, 16), (2, 32), (4, 64), (8, 16), (3, 128), (1, 64)][g.integers(6)]
+    dtype = ["f32", "f16", "bf16"][g.integers(3)]
+    n, rp, ci = graph(int(g.integers(2, 10)), 50 + seed)
+    parts, pad = int(g.integers(2, 4)), 8 * int(g.integers(0, 4))
+    views, packed = fused(n, parts, h, d, dtype, 60 + seed, pad)
+    k, v = views[-2], views[-1]
+    kc, vc = packed[-2], packed[-1]
+    if parts == 3:
+        q, qc = views[0], packed[0]
+    else:
+        qc = W.cast(g.standard_normal((n, h, d), dtype=np.float32), dtype).cuda()
+        q = qc
+    rp_t, ci_t = torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda()
+    paths = [("gather", None), ("gather", True)] + ([("mfma", None)] if dtype != "f32" and d >= 32 else [])
+    for path, ws in paths:
+        rw = gsa.gattn_build_rowwindows(rp_t, ci_t, n) if path == "mfma" else None
+        got = gsa.gattn_forward(rp_t, ci_t, q, k, v, path=path, rw=rw, workspace=ws)
+        want = gsa.gattn_forward(rp_t, ci_t, qc, kc, vc, path=path, rw=rw, workspace=ws)
+        assert torch.equal(got, want), f"{path} ws={ws} H={h} D={d} {dtype} parts={parts} pad={pad}"
