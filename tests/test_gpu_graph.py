@@ -22,13 +22,20 @@ def gsa():
     return g
 
 
-@pytest.mark.parametrize("cfg,path,ws", [(2, "gather", None), (2, "gather", True), (3, "gather", None),
-                                         (3, "gather", True), (5, "mfma", None)],
-                         ids=["cfg2-node", "cfg2-balanced", "cfg3-node", "cfg3-balanced", "cfg5-mfma"])
-def test_graph_replays_match_eager(gsa, cfg, path, ws):
+@pytest.mark.parametrize("cfg,path,ws,kvi", [(2, "gather", None, False), (2, "gather", True, False),
+                                             (3, "gather", None, False), (3, "gather", True, False),
+                                             (5, "mfma", None, False), (3, "gather", True, True),
+                                             (5, "mfma", None, True)],
+                         ids=["cfg2-node", "cfg2-balanced", "cfg3-node", "cfg3-balanced", "cfg5-mfma",
+                              "cfg3-balanced-kv-interleaved", "cfg5-mfma-kv-interleaved"])
+def test_graph_replays_match_eager(gsa, cfg, path, ws, kvi):
     c = case(cfg)
     wl = c.wl
-    print(f"graph capture config {cfg} path {path} workspace {ws}", flush=True)
+    print(f"graph capture config {cfg} path {path} workspace {ws} kv interleaved {kvi}", flush=True)
+    k, v = c.k, c.v
+    if kvi:  # K and V as the halves of one [N, 2, H, D] buffer: strided row views
+        kv = torch.stack((c.k, c.v), dim=1)
+        k, v = kv[:, 0], kv[:, 1]
     b = gsa.CsrBuilder(c.n, wl.nnz, c.src.device)
     rw = None
     if path == "mfma":  # row windows once per graph, outside the graph (they synchronize)
@@ -38,7 +45,7 @@ def test_graph_replays_match_eager(gsa, cfg, path, ws):
 
     def step():
         b(c.src, c.dst)
-        return gsa.gattn_forward(b.row_ptr, b.col_idx, c.q, c.k, c.v, c.e, mode=wl.mode, scale=wl.scale,
+        return gsa.gattn_forward(b.row_ptr, b.col_idx, c.q, k, v, c.e, mode=wl.mode, scale=wl.scale,
                                  clip=wl.clip, eps=wl.eps, path=path, rw=rw, workspace=ws)
 
     ref = step().clone()
