@@ -30,6 +30,10 @@ HBM traffic when a profile of this kernel source is committed, and the CPU
 oracle on one thread and on every core of the host, whose outputs also check
 the rows of the timed GPU output they cover: the run fails on a mismatch).
 
+--partition picks the gather path's workgroup partition (default auto: the
+balanced one when the largest in-degree is above 32x the mean on a graph
+below 2^24 edges, the rule of the Python graph layer; else equal node counts).
+
 --variant picks the op (default: forward):
     e_out      the forward also writes the RTMScore per-edge update
     edge_ids   E stays in COO order and is read through the CSR's edge_perm
