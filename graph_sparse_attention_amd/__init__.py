@@ -580,8 +580,11 @@ class Graph:
     def skewed(self) -> bool:
         """Whether hubs would set the gather kernel's end under equal
         destination counts per workgroup (Graph.skewed_degrees on this
-        graph's sizes and largest in-degree)."""
-        return Graph.skewed_degrees(self.num_nodes, self.nnz, self.max_degree if self.num_nodes else 0)
+        graph's sizes and largest in-degree, which is read back only when
+        the sizes leave the rule open)."""
+        if Graph.skewed_degrees(self.num_nodes, self.nnz, 1 << 31) is False:
+            return False
+        return Graph.skewed_degrees(self.num_nodes, self.nnz, self.max_degree)
 
     @staticmethod
     def skewed_degrees(num_nodes: int, nnz: int, max_degree: int) -> bool:
